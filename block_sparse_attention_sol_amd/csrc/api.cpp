@@ -1,0 +1,231 @@
+// api.cpp -- the C ABI of libsolattn (declared in include/solattn.h): argument validation,
+// workspace carving and kernel launches on the caller's stream.
+//
+// Every argument check happens before the first HIP call, so invalid calls return an error code
+// without touching the device.  No call allocates, frees or synchronises device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.hpp"
+#include "solattn.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return SOL_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t n_blocks(int64_t N, int block) { return (N + block - 1) / block; }
+int64_t padded_blocks(int64_t N, int block) { return (n_blocks(N, block) + 31) / 32 * 32; }
+
+// Offsets of the workspace regions (all 256-byte aligned).
+struct Workspace {
+  size_t kbar, kglob, kp, vbt, total;
+};
+
+Workspace layout(const sol_shape& s, int block) {
+  const int64_t BH = s.B * s.H;
+  const int64_t M = n_blocks(s.N, block);
+  const int64_t Mp = padded_blocks(s.N, block);
+  Workspace w{};
+  w.kbar = 0;
+  w.kglob = w.kbar + align_up((size_t)(BH * M * s.d) * sizeof(float));
+  w.kp = w.kglob + align_up((size_t)(BH * s.d) * sizeof(float));
+  w.vbt = w.kp + align_up((size_t)(3 * BH * Mp * s.d) * sizeof(uint16_t));
+  w.total = w.vbt + align_up((size_t)(2 * BH * s.d * Mp) * sizeof(uint16_t));
+  return w;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_shape(const sol_shape* s) {
+  if (!s) return fail(SOL_EINVAL, "shape is NULL");
+  if (s->B < 1 || s->H < 1) return fail(SOL_EINVAL, "B and H must be >= 1 (got B=%lld H=%lld)",
+                                        (long long)s->B, (long long)s->H);
+  if (s->N < 1 || s->N > (int64_t(1) << 30))
+    return fail(SOL_EINVAL, "N must be in [1, 2^30] (got %lld)", (long long)s->N);
+  if (s->B * s->H > 65535) return fail(SOL_EINVAL, "B*H must be <= 65535 (got %lld)",
+                                       (long long)(s->B * s->H));
+  if (s->d != 64 && s->d != 128)
+    return fail(SOL_EUNSUPPORTED, "d must be 64 or 128 (got %lld)", (long long)s->d);
+  const int64_t tiles = (s->N + SOL_QUERY_TILE - 1) / SOL_QUERY_TILE;
+  if (s->B * s->H * tiles > (int64_t)INT32_MAX)
+    return fail(SOL_EINVAL, "B*H*ceil(N/%d) exceeds the launch grid", SOL_QUERY_TILE);
+  return SOL_OK;
+}
+
+int check_block(int block) {
+  if (block != 64 && block != 128)
+    return fail(SOL_EUNSUPPORTED, "block must be 64 or 128 (got %d)", block);
+  return SOL_OK;
+}
+
+int check_tensor(const void* p, const char* name) {
+  if (!p) return fail(SOL_EINVAL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(SOL_EINVAL, "%s is not 16-byte aligned", name);
+  return SOL_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SOL_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sol_version(void) { return "libsolattn 0.1 (gfx950)"; }
+
+const char* sol_status_str(int status) {
+  switch (status) {
+    case SOL_OK: return "ok";
+    case SOL_EINVAL: return "invalid argument";
+    case SOL_EUNSUPPORTED: return "unsupported head dimension or block size";
+    case SOL_EWORKSPACE: return "workspace missing or too small";
+    case SOL_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* sol_last_error(void) { return g_last_error; }
+
+size_t sol_attn_workspace_bytes(const sol_shape* shape, int block) {
+  if (check_shape(shape) != SOL_OK || check_block(block) != SOL_OK) return 0;
+  return layout(*shape, block).total;
+}
+
+int sol_pool_kv(const sol_shape* shape, const void* k, const void* v, int block, float* kbar,
+                float* vbar, void* stream) {
+  int st;
+  if ((st = check_shape(shape)) || (st = check_block(block))) return st;
+  if ((st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
+      (st = check_tensor(kbar, "kbar")) || (st = check_tensor(vbar, "vbar")))
+    return st;
+  const int64_t BH = shape->B * shape->H;
+  const int64_t M = n_blocks(shape->N, block);
+  const size_t pooled = (size_t)(BH * M * shape->d) * sizeof(float);
+  if (overlaps(kbar, pooled, vbar, pooled)) return fail(SOL_EINVAL, "kbar and vbar overlap");
+  return hip_status(solattn::launch_pool((int)shape->d, BH, shape->N, block, k, v, kbar, vbar,
+                                         nullptr, nullptr, 0, (hipStream_t)stream),
+                    "pool kernel launch");
+}
+
+int sol_attn_fwd_ex(const sol_shape* shape, const void* q, const void* k, const void* v,
+                    float beta, int block, void* out, void* workspace, size_t workspace_bytes,
+                    const sol_attn_debug* dbg, void* stream) {
+  int st;
+  if ((st = check_shape(shape)) || (st = check_block(block))) return st;
+  if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
+      (st = check_tensor(out, "out")))
+    return st;
+  if (std::isnan(beta)) return fail(SOL_EINVAL, "beta is NaN");
+  const Workspace w = layout(*shape, block);
+  if (!workspace) return fail(SOL_EWORKSPACE, "workspace is NULL (need %zu bytes)", w.total);
+  if (!aligned16(workspace)) return fail(SOL_EINVAL, "workspace is not 16-byte aligned");
+  if (workspace_bytes < w.total)
+    return fail(SOL_EWORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, w.total);
+  const size_t tensor = (size_t)(shape->B * shape->H * shape->N * shape->d) * 2;
+  if (overlaps(out, tensor, q, tensor) || overlaps(out, tensor, k, tensor) ||
+      overlaps(out, tensor, v, tensor) || overlaps(out, tensor, workspace, w.total))
+    return fail(SOL_EINVAL, "out overlaps an input or the workspace");
+  if (dbg) {
+    const void* opt[] = {dbg->mask, dbg->mu,  dbg->sigma,    dbg->tau,
+                         dbg->lse,  dbg->tile_kept, dbg->out_f32};
+    for (const void* p : opt)
+      if (p && ((uintptr_t)p & 3u)) return fail(SOL_EINVAL, "debug output not 4-byte aligned");
+    if (dbg->out_f32 && !aligned16(dbg->out_f32))
+      return fail(SOL_EINVAL, "out_f32 is not 16-byte aligned");
+  }
+
+  const int d = (int)shape->d;
+  const int64_t BH = shape->B * shape->H;
+  const int64_t M = n_blocks(shape->N, block);
+  const int64_t Mp = padded_blocks(shape->N, block);
+  unsigned char* ws = (unsigned char*)workspace;
+  float* kbar = (float*)(ws + w.kbar);
+  float* kglob = (float*)(ws + w.kglob);
+  uint16_t* kp = (uint16_t*)(ws + w.kp);
+  uint16_t* vbt = (uint16_t*)(ws + w.vbt);
+  hipStream_t s = (hipStream_t)stream;
+
+  hipError_t e = solattn::launch_pool(d, BH, shape->N, block, k, v, kbar, nullptr, kp, vbt, Mp, s);
+  if (e != hipSuccess) return hip_status(e, "pool kernel launch");
+  e = solattn::launch_kglob(d, BH, M, kbar, kglob, s);
+  if (e != hipSuccess) return hip_status(e, "kglob kernel launch");
+
+  solattn::SparseArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.out = (uint16_t*)out;
+  a.kp = kp;
+  a.vbt = vbt;
+  a.kglob = kglob;
+  a.BH = BH;
+  a.N = shape->N;
+  a.M = M;
+  a.Mp = Mp;
+  a.block = block;
+  a.beta = beta;
+  if (dbg) {
+    a.drop = dbg->drop_unselected ? 1 : 0;
+    a.mask = dbg->mask;
+    a.mu = dbg->mu;
+    a.sigma = dbg->sigma;
+    a.tau = dbg->tau;
+    a.lse = dbg->lse;
+    a.tile_kept = dbg->tile_kept;
+    a.out_f32 = dbg->out_f32;
+  }
+  return hip_status(solattn::launch_sparse(d, a, s), "sparse attention kernel launch");
+}
+
+int sol_attn_fwd(const sol_shape* shape, const void* q, const void* k, const void* v, float beta,
+                 int block, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return sol_attn_fwd_ex(shape, q, k, v, beta, block, out, workspace, workspace_bytes, nullptr,
+                         stream);
+}
+
+int sol_dense_fwd(const sol_shape* shape, const void* q, const void* k, const void* v, void* out,
+                  float* lse, void* stream) {
+  int st;
+  if ((st = check_shape(shape))) return st;
+  if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
+      (st = check_tensor(out, "out")))
+    return st;
+  if (lse && ((uintptr_t)lse & 3u)) return fail(SOL_EINVAL, "lse not 4-byte aligned");
+  const size_t tensor = (size_t)(shape->B * shape->H * shape->N * shape->d) * 2;
+  if (overlaps(out, tensor, q, tensor) || overlaps(out, tensor, k, tensor) ||
+      overlaps(out, tensor, v, tensor))
+    return fail(SOL_EINVAL, "out overlaps an input");
+  return hip_status(solattn::launch_dense((int)shape->d, shape->B * shape->H, shape->N, q, k, v,
+                                          out, lse, (hipStream_t)stream),
+                    "dense attention kernel launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// common.hpp -- shared device helpers for the gfx950 kernels of libsolattn.
+//
+// Matrix-core conventions (CDNA4 v_mfma_f32_32x32x16_bf16, one wave of 64 lanes):
+//   lane l = 32*h + c  (h = l >> 5 is the lane half, c = l & 31).
+//   A operand (32 x 16): lane l holds 8 bf16 of row c; B operand (16 x 32): 8 bf16 of column c.
+//   Both operands use the same (half, slot) -> k assignment, so any consistent choice of which 8 of
+//   the 16 k indices a half holds gives the same product; the kernels pick the k indices per half
+//   to suit their data (contiguous head-dim chunks for Q.K, and the score layout for P.V).
+//   Result (32 x 32, 16 fp32 per lane): lane l holds column c, rows 8*(v/4) + 4*h + (v%4), v=0..15.
+// The attention kernels compute S^T = K Q^T so that one lane owns one query (column): the
+// softmax row statistics are then lane-local plus one exchange with the other lane half.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace solattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kQTile = 128;           // query rows per workgroup tile
+constexpr int kWaves = 4;             // waves per workgroup; each wave owns 32 query rows
+constexpr int kThreads = kWave * kWaves;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// bf16 <-> fp32 bit helpers (round to nearest even; inputs here are finite).
+__device__ __forceinline__ uint32_t f32_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float bits_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return bits_f32(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return bits_f32(packed & 0xffff0000u); }
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = f32_bits(x);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Two fp32 -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+// acc + lo + hi of a packed bf16 pair, in fp32 (one v_dot2_f32_bf16 against (1, 1)): sums
+// exactly the rounded values that enter the matrix product.
+__device__ __forceinline__ float add_bf16x2(uint32_t packed, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
+}
+
+// Exchange a value with the lane in the other half of the wave (l <-> l ^ 32).
+__device__ __forceinline__ float swap_halves(float x) {
+  return __shfl_xor(x, 32, kWave);
+}
+__device__ __forceinline__ uint32_t swap_halves_u(uint32_t x) {
+  return (uint32_t)__shfl_xor((int)x, 32, kWave);
+}
+
+// LDS row-major tile with rows of `kChunks` 16-byte chunks; chunk index XOR-swizzled by the row so
+// that 8 consecutive rows read at the same logical chunk hit 8 distinct bank groups.
+template <int kChunks>
+__device__ __forceinline__ int swz16(int row, int chunk) {
+  return row * kChunks + (chunk ^ (row & 7));
+}
+
+// Transposed V tile in LDS: Vt[d][key], rows of kSlots 8-byte slots (4 bf16 keys each), slot index
+// XOR-swizzled by the row so 16 consecutive d rows reading one logical slot are conflict-free.
+template <int kSlots>
+__device__ __forceinline__ int swz8(int row, int slot) {
+  return row * kSlots + (slot ^ (row & 15));
+}
+
+}  // namespace solattn

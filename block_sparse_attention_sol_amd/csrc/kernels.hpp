@@ -1,0 +1,43 @@
+// kernels.hpp -- host-side launchers of the gfx950 kernels (internal to libsolattn).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace solattn {
+
+// Pooled K/V of every key block.  kp / vbt (and Mp) only for the attention workspace; NULL in
+// the public pooling call.
+hipError_t launch_pool(int d, int64_t BH, int64_t N, int block, const void* k, const void* v,
+                       float* kbar, float* vbar, uint16_t* kp, uint16_t* vbt, int64_t Mp,
+                       hipStream_t stream);
+hipError_t launch_kglob(int d, int64_t BH, int64_t M, const float* kbar, float* kglob,
+                        hipStream_t stream);
+
+struct SparseArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;
+  const uint16_t* kp;   // [3][BH][Mp][d]
+  const uint16_t* vbt;  // [2][BH][d][Mp] (hi, lo)
+  const float* kglob;   // [BH][d]
+  int64_t BH, N, M, Mp;
+  int block;
+  float beta;
+  int drop;
+  // optional outputs
+  uint32_t* mask;
+  float* mu;
+  float* sigma;
+  float* tau;
+  float* lse;
+  int32_t* tile_kept;
+  float* out_f32;
+};
+hipError_t launch_sparse(int d, const SparseArgs& a, hipStream_t stream);
+
+hipError_t launch_dense(int d, int64_t BH, int64_t N, const void* q, const void* k, const void* v,
+                        void* out, float* lse, hipStream_t stream);
+
+}  // namespace solattn

@@ -1,0 +1,225 @@
+"""Thin Python binding of libsolattn (ctypes over torch device tensors).
+
+Argument marshalling only: every step of the forward pass runs in the HIP kernels of
+libsolattn.so.  Names follow include/solattn.h.  The library must have been built
+(``python -m block_sparse_attention_sol_amd.build``); there is no fallback -- a missing library
+or a missing GPU raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libsolattn.so")
+
+SOL_OK = 0
+SOL_EINVAL = -1
+SOL_EUNSUPPORTED = -2
+SOL_EWORKSPACE = -3
+SOL_EHIP = -4
+QUERY_TILE = 128
+
+# Every symbol include/solattn.h declares.
+EXPORTS = (
+    "sol_attn_workspace_bytes",
+    "sol_pool_kv",
+    "sol_attn_fwd",
+    "sol_attn_fwd_ex",
+    "sol_dense_fwd",
+    "sol_status_str",
+    "sol_last_error",
+    "sol_version",
+)
+
+
+class SolShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("d", ctypes.c_int64)]
+
+
+class SolAttnDebug(ctypes.Structure):
+    _fields_ = [("mask", ctypes.c_void_p), ("mu", ctypes.c_void_p), ("sigma", ctypes.c_void_p),
+                ("tau", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("tile_kept", ctypes.c_void_p),
+                ("out_f32", ctypes.c_void_p), ("drop_unselected", ctypes.c_int)]
+
+
+class SolError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libsolattn error {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libsolattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it with `python -m block_sparse_attention_sol_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, sz, ci, cf = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_float
+    shp = ctypes.POINTER(SolShape)
+    lib.sol_attn_workspace_bytes.argtypes = [shp, ci]
+    lib.sol_attn_workspace_bytes.restype = sz
+    lib.sol_pool_kv.argtypes = [shp, vp, vp, ci, vp, vp, vp]
+    lib.sol_attn_fwd.argtypes = [shp, vp, vp, vp, cf, ci, vp, vp, sz, vp]
+    lib.sol_attn_fwd_ex.argtypes = [shp, vp, vp, vp, cf, ci, vp, vp, sz,
+                                    ctypes.POINTER(SolAttnDebug), vp]
+    lib.sol_dense_fwd.argtypes = [shp, vp, vp, vp, vp, vp, vp]
+    for f in ("sol_pool_kv", "sol_attn_fwd", "sol_attn_fwd_ex", "sol_dense_fwd"):
+        getattr(lib, f).restype = ci
+    lib.sol_status_str.argtypes = [ci]
+    lib.sol_status_str.restype = ctypes.c_char_p
+    lib.sol_last_error.argtypes = []
+    lib.sol_last_error.restype = ctypes.c_char_p
+    lib.sol_version.argtypes = []
+    lib.sol_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != SOL_OK:
+        lib = load_library()
+        raise SolError(status, lib.sol_last_error().decode() or lib.sol_status_str(status).decode())
+
+
+def _shape(q) -> SolShape:
+    B, H, N, d = q.shape
+    return SolShape(B, H, N, d)
+
+
+def _dev(t, name):
+    import torch
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def n_blocks(N: int, block: int) -> int:
+    return (N + block - 1) // block
+
+
+def workspace_bytes(shape, block: int) -> int:
+    """Workspace size for a [B, H, N, d] shape (tuple or tensor)."""
+    lib = load_library()
+    B, H, N, d = tuple(shape.shape) if hasattr(shape, "shape") else tuple(shape)
+    return int(lib.sol_attn_workspace_bytes(ctypes.byref(SolShape(B, H, N, d)), block))
+
+
+def new_workspace(shape, block: int, device="cuda"):
+    import torch
+    return torch.empty(max(workspace_bytes(shape, block), 1), dtype=torch.uint8, device=device)
+
+
+def pool_kv(k, v, block: int, stream=None):
+    """Block means of K and V: fp32 [B, H, M, d] each."""
+    import torch
+    lib = load_library()
+    B, H, N, d = k.shape
+    M = n_blocks(N, block)
+    kbar = torch.empty((B, H, M, d), dtype=torch.float32, device=k.device)
+    vbar = torch.empty_like(kbar)
+    _check(lib.sol_pool_kv(ctypes.byref(_shape(k)), _dev(k, "k"), _dev(v, "v"), block,
+                           _dev(kbar, "kbar"), _dev(vbar, "vbar"), _stream(stream)))
+    return kbar, vbar
+
+
+def attn_fwd(q, k, v, beta: float, block: int, out=None, workspace=None, debug: bool = False,
+             drop_unselected: bool = False, stream=None):
+    """Sol-Attn forward.  Returns out, or (out, dict of debug outputs) when debug/drop is set."""
+    import torch
+    lib = load_library()
+    B, H, N, d = q.shape
+    for t, n in ((k, "k"), (v, "v")):
+        if t.shape != q.shape or t.dtype != torch.bfloat16:
+            raise ValueError(f"{n} must be bf16 with the shape of q")
+    if q.dtype != torch.bfloat16:
+        raise ValueError("q must be bf16")
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = new_workspace(q.shape, block, q.device)
+    shp = _shape(q)
+    if not debug and not drop_unselected:
+        _check(lib.sol_attn_fwd(ctypes.byref(shp), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+                                float(beta), block, _dev(out, "out"), _dev(workspace, "workspace"),
+                                workspace.numel(), _stream(stream)))
+        return out
+    M = n_blocks(N, block)
+    W = (M + 31) // 32
+    T = (N + QUERY_TILE - 1) // QUERY_TILE
+    dev = q.device
+    dbg = {}
+    dstruct = SolAttnDebug()
+    if debug:
+        dbg = {
+            "mask": torch.empty((B, H, N, W), dtype=torch.int32, device=dev),
+            "mu": torch.empty((B, H, N), dtype=torch.float32, device=dev),
+            "sigma": torch.empty((B, H, N), dtype=torch.float32, device=dev),
+            "tau": torch.empty((B, H, N), dtype=torch.float32, device=dev),
+            "lse": torch.empty((B, H, N), dtype=torch.float32, device=dev),
+            "tile_kept": torch.empty((B, H, T), dtype=torch.int32, device=dev),
+            "out_f32": torch.empty((B, H, N, d), dtype=torch.float32, device=dev),
+        }
+        for key, t in dbg.items():
+            setattr(dstruct, key, t.data_ptr())
+    dstruct.drop_unselected = int(bool(drop_unselected))
+    _check(lib.sol_attn_fwd_ex(ctypes.byref(shp), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+                               float(beta), block, _dev(out, "out"), _dev(workspace, "workspace"),
+                               workspace.numel(), ctypes.byref(dstruct), _stream(stream)))
+    return out, dbg
+
+
+def dense_fwd(q, k, v, out=None, want_lse: bool = False, stream=None):
+    """Dense attention softmax(q k^T / sqrt(d)) v.  Returns out (and lse if asked)."""
+    import torch
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if want_lse else None
+    _check(lib.sol_dense_fwd(ctypes.byref(_shape(q)), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+                             _dev(out, "out"), _dev(lse, "lse") if lse is not None else None,
+                             _stream(stream)))
+    return (out, lse) if want_lse else out
+
+
+def kept_block_flops(tile_kept, mask, N: int, d: int, block: int) -> float:
+    """Kept-block FLOPs F = 4*d*sum_t sum_{j kept by tile t} rows_t * n_j.
+
+    tile_kept [B, H, T] (blocks computed per query tile) and mask [B, H, N, W] are the kernel's own
+    debug outputs; the mask tells which tiles computed the (possibly partial) last block."""
+    import torch
+    T = tile_kept.shape[-1]
+    M = n_blocks(N, block)
+    n_last = N - (M - 1) * block
+    rows = torch.full((T,), float(QUERY_TILE), dtype=torch.float64, device=tile_kept.device)
+    rows[-1] = N - (T - 1) * QUERY_TILE
+    kept = tile_kept.to(torch.float64).reshape(-1, T)
+    units = (kept * block * rows).sum()
+    if n_last != block:
+        bit = (mask[..., (M - 1) // 32].to(torch.int64) >> ((M - 1) % 32)) & 1   # [B, H, N]
+        pad = T * QUERY_TILE - N
+        bit = torch.nn.functional.pad(bit.reshape(-1, N), (0, pad)).reshape(-1, T, QUERY_TILE)
+        last_kept = bit.amax(dim=2).to(torch.float64)                            # [BH, T]
+        units -= ((block - n_last) * last_kept * rows).sum()
+    return float(4.0 * d * units)
+
+
+def dense_flops(B: int, H: int, N: int, d: int) -> float:
+    return 4.0 * B * H * N * N * d

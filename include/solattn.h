@@ -1,0 +1,128 @@
+/*
+ * solattn.h -- C ABI of libsolattn: the Sol-Attn sparse attention forward pass on gfx950.
+ *
+ * The method is the one summarised on the page "Sol-Attn: Accelerating Video Generation
+ * Inference via On-the-Fly Attention Sparsification" (agihunt.info/papers/2607.24027):
+ *   - each query i scores every key block j with a pre-softmax proxy (paragraph on routing);
+ *   - the proxy row of query i gives a mean mu_i and a standard deviation sigma_i, and block j is
+ *     kept when its score clears tau_i = mu_i + beta * sigma_i, one beta for all queries
+ *     (paragraph on the per-query threshold);
+ *   - kept blocks get exact attention, unselected blocks are approximated rather than dropped,
+ *     all inside one online-softmax pass (paragraphs on the fused operator).
+ * The page leaves the proxy and the approximation open; this library fixes them as
+ *   proxy        s_ij = q_i . Kbar_j / sqrt(d),   Kbar_j = mean of the keys of block j;
+ *   approximation: each unselected block enters the softmax as one pooled token with logit
+ *                s_ij + ln(n_j) and value Vbar_j = mean of the values of block j (n_j = tokens);
+ *   statistics   mu_i and sigma_i over all M blocks, sigma the population standard deviation;
+ *   selection    kept iff s_ij >= tau_i; beta = -inf keeps all, +inf keeps none.
+ * The attention is bidirectional (no causal mask) and forward only, as the page's limitations
+ * paragraph states.
+ *
+ * Conventions shared by every call
+ *   Layout    q, k, v, out: contiguous [B][H][N][d] bf16 (raw uint16 bit patterns), device memory.
+ *   Blocks    key block j covers tokens [j*block, min((j+1)*block, N)); M = ceil(N / block).
+ *   Scale     1/sqrt(d), fixed.
+ *   Supported d in {64, 128}; block in {64, 128}; 1 <= N <= 2^30; B*H >= 1.
+ *   Pointers  all tensor pointers are device pointers, 16-byte aligned, owned by the caller.
+ *             The library never allocates or frees device memory and keeps no device state.
+ *             out must not overlap q, k, v or the workspace.
+ *   Streams   `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every call only
+ *             enqueues work on that stream and returns; nothing synchronises.  A fault inside a
+ *             kernel surfaces at the caller's next synchronisation of the stream.
+ *   Errors    calls return SOL_OK (0) or a negative sol_status.  Argument errors are detected
+ *             before any HIP call is made (so they are testable without a GPU); the thread-local
+ *             message from sol_last_error() says which argument.  A failed kernel launch returns
+ *             SOL_EHIP.  No C++ exception crosses this interface.
+ */
+#ifndef SOLATTN_H
+#define SOLATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sol_status {
+  SOL_OK = 0,
+  SOL_EINVAL = -1,        /* NULL/misaligned pointer, bad size, NaN beta */
+  SOL_EUNSUPPORTED = -2,  /* d or block outside the supported set */
+  SOL_EWORKSPACE = -3,    /* workspace NULL or smaller than sol_attn_workspace_bytes() */
+  SOL_EHIP = -4           /* the HIP runtime reported an error at launch */
+} sol_status;
+
+/* Tensor extents: batch, heads, tokens, head dimension. */
+typedef struct sol_shape {
+  int64_t B, H, N, d;
+} sol_shape;
+
+/* Query rows handled together by one tile of the fused kernel.  A key block is computed for a
+ * tile when any row of the tile keeps it (rows that do not keep it are masked inside the tile). */
+#define SOL_QUERY_TILE 128
+
+/* Bytes of device workspace sol_attn_fwd needs for this shape and block size (0 on bad input).
+ * Holds the pooled keys/values and their bf16 split copies; contents are scratch between calls. */
+size_t sol_attn_workspace_bytes(const sol_shape* shape, int block);
+
+/*
+ * K/V mean pooling: kbar[b][h][j][:] = (1/n_j) * sum of k[b][h][t][:] over the tokens t of block j,
+ * and likewise vbar from v.  Sums in fp32, true division by n_j.
+ *   k, v        [B][H][N][d] bf16, device.
+ *   kbar, vbar  [B][H][M][d] fp32, device, written.
+ * The proxy of the page's routing paragraph is the dot product of a query with kbar.
+ */
+int sol_pool_kv(const sol_shape* shape, const void* k, const void* v, int block, float* kbar,
+                float* vbar, void* stream);
+
+/*
+ * Sol-Attn forward: out = the softmax over {exact keys of kept blocks} U {one pooled token per
+ * unselected block}, per query row, as defined at the top of this header.
+ *   q, k, v     [B][H][N][d] bf16, device.
+ *   beta        global threshold offset; finite or +-infinity; NaN -> SOL_EINVAL.
+ *   block       key block size (tokens per block).
+ *   out         [B][H][N][d] bf16, device, written.
+ *   workspace   device scratch of at least sol_attn_workspace_bytes(shape, block) bytes.
+ */
+int sol_attn_fwd(const sol_shape* shape, const void* q, const void* k, const void* v, float beta,
+                 int block, void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Optional outputs of sol_attn_fwd_ex (every pointer may be NULL; device memory). */
+typedef struct sol_attn_debug {
+  uint32_t* mask;      /* [B][H][N][ceil(M/32)]: bit j%32 of word j/32 set iff query keeps block j */
+  float* mu;           /* [B][H][N] row mean of the proxy scores */
+  float* sigma;        /* [B][H][N] row population standard deviation */
+  float* tau;          /* [B][H][N] threshold mu + beta*sigma (+-inf for infinite beta) */
+  float* lse;          /* [B][H][N] natural log of the softmax denominator (with its max) */
+  int32_t* tile_kept;  /* [B][H][ceil(N/SOL_QUERY_TILE)] key blocks computed for each query tile */
+  float* out_f32;      /* [B][H][N][d] the output before its final rounding to bf16 (out is the
+                          round-to-nearest-even bf16 of these values) */
+  int drop_unselected; /* 0: the method.  1: ablation -- unselected blocks are dropped instead of
+                          pooled (a row with nothing kept then outputs 0 and lse = -inf). */
+} sol_attn_debug;
+
+/* sol_attn_fwd plus the optional outputs above (dbg may be NULL, then identical to sol_attn_fwd). */
+int sol_attn_fwd_ex(const sol_shape* shape, const void* q, const void* k, const void* v,
+                    float beta, int block, void* out, void* workspace, size_t workspace_bytes,
+                    const sol_attn_debug* dbg, void* stream);
+
+/*
+ * Dense reference attention: out = softmax(q k^T / sqrt(d)) v over all N keys, no mask.  The
+ * speedup of the sparse pass is measured against this.
+ *   q, k, v, out  [B][H][N][d] bf16, device.   lse  [B][H][N] fp32, device, or NULL.
+ */
+int sol_dense_fwd(const sol_shape* shape, const void* q, const void* k, const void* v, void* out,
+                  float* lse, void* stream);
+
+/* Static text for a status code. */
+const char* sol_status_str(int status);
+/* Message for the last error returned on the calling thread ("" if none). */
+const char* sol_last_error(void);
+/* Library version string. */
+const char* sol_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SOLATTN_H */
