@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the Sol-Attn forward pass on one MI355X (one process, one GPU).
+
+A step is one pass of the whole hot path over the workload: sol_attn_fwd (K/V pooling, pooled-key
+mean, fused routing + pooled-token + exact-attention kernel) followed by sol_dense_fwd, the dense
+reference the speedup is measured against, on the same resident tensors.
+
+Printed: one JSON line.  value = effective TFLOP/s of the sparse forward: kept-block FLOPs
+F = 4*d*sum over query tiles t of sum over kept blocks j of rows_t*n_j, divided by its latency.
+Extra fields give the dense latency, the speedup, densities, per-kernel times, the roofline of the
+fused kernel (live HIP events on the launch stream) and the fp64 CPU oracle timed on a bounded
+sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload wan] [--beta B] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse attn fwd ms + eff. TFLOPS & speedup vs own dense, N=75600 h40 d128"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg: str):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def calibrate_beta(sol, q, k, v, block, target, ws, out):
+    """Bisection on beta so that the kept-block density at query-tile granularity hits target
+    (density is non-increasing in beta)."""
+    import torch
+    M = sol.n_blocks(q.shape[2], block)
+
+    def density(beta):
+        _, dbg = sol.attn_fwd(q, k, v, beta, block, out=out, workspace=ws, debug=True)
+        tk = dbg["tile_kept"]
+        return float(tk.sum().item()) / (tk.numel() * M)
+
+    lo, hi = 0.0, 4.0
+    d_lo, d_hi = density(lo), density(hi)
+    while d_hi > target and hi < 16:
+        lo, hi = hi, hi * 2
+        d_hi = density(hi)
+    for _ in range(18):
+        mid = 0.5 * (lo + hi)
+        dm = density(mid)
+        if dm > target:
+            lo = mid
+        else:
+            hi = mid
+        if abs(dm - target) < 2e-4:
+            return mid
+    torch.cuda.synchronize()
+    return 0.5 * (lo + hi)
+
+
+def cpu_baseline(w, q, k, v, beta, F_tile, seconds=12.0):
+    """The fp64 oracle on a bounded, seeded sample of query rows of head 0, scaled to the same
+    effective-TFLOP/s unit as the GPU value (F_tile x sampled fraction / oracle seconds)."""
+    import numpy as np
+    from oracle import oracle
+    qh, kh, vh = (t[0, 0].float().cpu().numpy() for t in (q, k, v))
+    N = w.N
+    total_rows = w.B * w.H * N
+    rng = np.random.default_rng(0)
+    probe = np.sort(rng.choice(N, size=512, replace=False))
+    t0 = time.perf_counter()
+    oracle.attn_rows(qh, kh, vh, beta, w.block, rows=probe)
+    per_row = (time.perf_counter() - t0) / probe.size
+    n = int(min(N, max(1024, seconds / max(per_row, 1e-9))))
+    rows = np.sort(rng.choice(N, size=n, replace=False))
+    t0 = time.perf_counter()
+    oracle.attn_rows(qh, kh, vh, beta, w.block, rows=rows)
+    dt = time.perf_counter() - t0
+    frac = n / total_rows
+    return {
+        "value": F_tile * frac / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"{n} of {total_rows} query rows (head 0, seeded uniform), full method per row, "
+                  f"{dt:.1f} s; value = kept-block FLOPs x {frac:.3e} / seconds",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan")
+    ap.add_argument("--beta", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (calibrates the HBM "
+                         "byte counters of a profiler run) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the Sol-Attn forward is measured per GPU (heads "
+              "shard with no communication); --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_attention_sol_amd import solattn as sol
+    from block_sparse_attention_sol_amd import synth
+
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+        return
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sol.load_library()
+    w = synth.WORKLOADS[args.workload]
+    target = w.target_density[0] if w.target_density else None
+    log(f"workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} block={w.block}; generating")
+    q, k, v = (t.cuda() for t in synth.generate(w))
+    B, H, N, d = q.shape
+    out = torch.empty_like(q)
+    dout = torch.empty_like(q)
+    ws = sol.new_workspace(q.shape, w.block)
+
+    if args.beta is not None:
+        beta = args.beta
+    elif target is not None:
+        beta = calibrate_beta(sol, q, k, v, w.block, target, ws, out)
+    else:
+        beta = w.betas[0]
+    _, dbg = sol.attn_fwd(q, k, v, beta, w.block, out=out, workspace=ws, debug=True)
+    torch.cuda.synchronize()
+    M = sol.n_blocks(N, w.block)
+    T = (N + sol.QUERY_TILE - 1) // sol.QUERY_TILE
+    kept_blocks = int(dbg["tile_kept"].sum().item())
+    rho_tile = kept_blocks / (B * H * T * M)
+    F_tile = sol.kept_block_flops(dbg["tile_kept"], dbg["mask"], N, d, w.block)
+    mask = dbg["mask"].view(torch.int32)
+    row_bits = sum(int(torch.bitwise_and(torch.bitwise_right_shift(mask, s), 1).sum().item())
+                   for s in range(32))
+    rho_row = row_bits / (B * H * N * M)
+    del dbg
+    log(f"beta={beta:.4f} rho_tile={rho_tile:.4f} rho_row={rho_row:.4f} F_tile={F_tile / 1e12:.2f} TF")
+
+    K, Wm = args.steps, args.warmup
+    ev = sol.HipEvents(4 * (K + Wm))
+    dense_start = [torch.cuda.Event(enable_timing=True) for _ in range(K + Wm)]
+    dense_end = [torch.cuda.Event(enable_timing=True) for _ in range(K + Wm)]
+
+    def step(i):
+        sol.attn_fwd(q, k, v, beta, w.block, out=out, workspace=ws,
+                     events=ev.handles[4 * i: 4 * i + 4])
+        dense_start[i].record()
+        sol.dense_fwd(q, k, v, out=dout)
+        dense_end[i].record()
+
+    for i in range(Wm):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(Wm, Wm + K):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    idx = range(Wm, Wm + K)
+    pool_ms = [ev.elapsed_ms(4 * i, 4 * i + 1) for i in idx]
+    kglob_ms = [ev.elapsed_ms(4 * i + 1, 4 * i + 2) for i in idx]
+    fused_ms = [ev.elapsed_ms(4 * i + 2, 4 * i + 3) for i in idx]
+    sparse_ms = [ev.elapsed_ms(4 * i, 4 * i + 3) for i in idx]
+    dense_ms = [dense_start[i].elapsed_time(dense_end[i]) for i in idx]
+    avg = lambda xs: sum(xs) / len(xs)
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    t_sparse, t_dense, t_fused, t_pool = avg(sparse_ms), avg(dense_ms), avg(fused_ms), avg(pool_ms)
+
+    dense_F = sol.dense_flops(B, H, N, d)
+    pool_bytes = 2 * B * H * N * d * 2 + 2 * B * H * M * d * 4  # K,V read + Kbar,Vbar (fp32) written
+    achieved = F_tile / (t_fused * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": F_tile / (t_sparse * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": wall * 1e3 / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.grid[0]}x{w.grid[1]}x{w.grid[2]} latent grid, positional amplitude "
+                        f"{w.amp_range or w.amp}, seed 0",
+            "B": B, "H": H, "N": N, "d": d, "block": w.block, "beta": round(beta, 5),
+            "target_kept_block_density": target, "query_tile": sol.QUERY_TILE,
+            "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)",
+        },
+        "sparse_ms": t_sparse,
+        "sparse_ms_median": med(sparse_ms),
+        "dense_ms": t_dense,
+        "speedup_vs_dense": t_dense / t_sparse,
+        "dense_tflops": dense_F / (t_dense * 1e-3) / 1e12,
+        "dense_mfma_frac": dense_F / (t_dense * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "kernel_ms": {"pool_kv": t_pool, "kbar_mean": avg(kglob_ms), "fused": t_fused},
+        "rho_tile": rho_tile,
+        "rho_row": rho_row,
+        "kept_block_tflop": F_tile / 1e12,
+        "pool_gbs": pool_bytes / (t_pool * 1e-3) / 1e9,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": None,
+            "kernel": "sol_attn_kernel<128,128> (fused routing + pooled tokens + exact attention)",
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, beta, F_tile)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

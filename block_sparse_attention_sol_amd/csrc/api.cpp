@@ -39,7 +39,7 @@ int64_t padded_blocks(int64_t N, int block) { return (n_blocks(N, block) + 31) /
 
 // Offsets of the workspace regions (all 256-byte aligned).
 struct Workspace {
-  size_t kbar, kglob, kp, vbt, total;
+  size_t kbar, kglob, kglob64, cp, kp, vbp, tau, rowmask, total;
 };
 
 Workspace layout(const sol_shape& s, int block) {
@@ -49,9 +49,13 @@ Workspace layout(const sol_shape& s, int block) {
   Workspace w{};
   w.kbar = 0;
   w.kglob = w.kbar + align_up((size_t)(BH * M * s.d) * sizeof(float));
-  w.kp = w.kglob + align_up((size_t)(BH * s.d) * sizeof(float));
-  w.vbt = w.kp + align_up((size_t)(3 * BH * Mp * s.d) * sizeof(uint16_t));
-  w.total = w.vbt + align_up((size_t)(2 * BH * s.d * Mp) * sizeof(uint16_t));
+  w.kglob64 = w.kglob + align_up((size_t)(BH * s.d) * sizeof(float));
+  w.cp = w.kglob64 + align_up((size_t)(BH * s.d) * sizeof(double));
+  w.kp = w.cp + align_up((size_t)(3 * BH * s.d * s.d) * sizeof(uint16_t));
+  w.vbp = w.kp + align_up((size_t)(3 * BH * Mp * s.d) * sizeof(uint16_t));
+  w.tau = w.vbp + align_up((size_t)(2 * BH * Mp * s.d) * sizeof(uint16_t));
+  w.rowmask = w.tau + align_up((size_t)(BH * s.N) * sizeof(float));
+  w.total = w.rowmask + align_up((size_t)(BH * s.N * (Mp / 32)) * sizeof(uint32_t));
   return w;
 }
 
@@ -61,8 +65,8 @@ int check_shape(const sol_shape* s) {
   if (!s) return fail(SOL_EINVAL, "shape is NULL");
   if (s->B < 1 || s->H < 1) return fail(SOL_EINVAL, "B and H must be >= 1 (got B=%lld H=%lld)",
                                         (long long)s->B, (long long)s->H);
-  if (s->N < 1 || s->N > (int64_t(1) << 30))
-    return fail(SOL_EINVAL, "N must be in [1, 2^30] (got %lld)", (long long)s->N);
+  if (s->N < 1 || s->N > (int64_t(1) << 22))
+    return fail(SOL_EINVAL, "N must be in [1, 2^22] (got %lld)", (long long)s->N);
   if (s->B * s->H > 65535) return fail(SOL_EINVAL, "B*H must be <= 65535 (got %lld)",
                                        (long long)(s->B * s->H));
   if (s->d != 64 && s->d != 128)
@@ -169,14 +173,41 @@ int sol_attn_fwd_ex(const sol_shape* shape, const void* q, const void* k, const 
   unsigned char* ws = (unsigned char*)workspace;
   float* kbar = (float*)(ws + w.kbar);
   float* kglob = (float*)(ws + w.kglob);
+  double* kglob64 = (double*)(ws + w.kglob64);
+  uint16_t* cp = (uint16_t*)(ws + w.cp);
   uint16_t* kp = (uint16_t*)(ws + w.kp);
-  uint16_t* vbt = (uint16_t*)(ws + w.vbt);
+  uint16_t* vbp = (uint16_t*)(ws + w.vbp);
+  float* tau = (float*)(ws + w.tau);
+  uint32_t* rowmask = (dbg && dbg->mask) ? dbg->mask : (uint32_t*)(ws + w.rowmask);
   hipStream_t s = (hipStream_t)stream;
 
-  hipError_t e = solattn::launch_pool(d, BH, shape->N, block, k, v, kbar, nullptr, kp, vbt, Mp, s);
+  auto mark = [&](int i) -> hipError_t {
+    if (dbg && dbg->events[i]) return hipEventRecord((hipEvent_t)dbg->events[i], s);
+    return hipSuccess;
+  };
+  hipError_t e = mark(0);
+  if (e != hipSuccess) return hip_status(e, "event record");
+  e = solattn::launch_pool(d, BH, shape->N, block, k, v, kbar, nullptr, kp, vbp, Mp, s);
   if (e != hipSuccess) return hip_status(e, "pool kernel launch");
-  e = solattn::launch_kglob(d, BH, M, kbar, kglob, s);
-  if (e != hipSuccess) return hip_status(e, "kglob kernel launch");
+  if ((e = mark(1)) != hipSuccess) return hip_status(e, "event record");
+  e = solattn::launch_kstats(d, BH, M, kbar, kglob, kglob64, cp, s);
+  if (e != hipSuccess) return hip_status(e, "pooled-key statistics launch");
+  solattn::RowStatsArgs r{};
+  r.q = (const uint16_t*)q;
+  r.cp = cp;
+  r.kglob = kglob;
+  r.BH = BH;
+  r.N = shape->N;
+  r.beta = beta;
+  r.tau = tau;
+  if (dbg) {
+    r.mu = dbg->mu;
+    r.sigma = dbg->sigma;
+    r.tau_out = dbg->tau;
+  }
+  e = solattn::launch_rowstats(d, r, s);
+  if (e != hipSuccess) return hip_status(e, "row statistics launch");
+  if ((e = mark(2)) != hipSuccess) return hip_status(e, "event record");
 
   solattn::SparseArgs a{};
   a.q = (const uint16_t*)q;
@@ -184,25 +215,23 @@ int sol_attn_fwd_ex(const sol_shape* shape, const void* q, const void* k, const 
   a.v = (const uint16_t*)v;
   a.out = (uint16_t*)out;
   a.kp = kp;
-  a.vbt = vbt;
-  a.kglob = kglob;
+  a.vbp = vbp;
+  a.tau = tau;
+  a.rowmask = rowmask;
   a.BH = BH;
   a.N = shape->N;
   a.M = M;
   a.Mp = Mp;
   a.block = block;
-  a.beta = beta;
   if (dbg) {
     a.drop = dbg->drop_unselected ? 1 : 0;
-    a.mask = dbg->mask;
-    a.mu = dbg->mu;
-    a.sigma = dbg->sigma;
-    a.tau = dbg->tau;
     a.lse = dbg->lse;
     a.tile_kept = dbg->tile_kept;
     a.out_f32 = dbg->out_f32;
   }
-  return hip_status(solattn::launch_sparse(d, a, s), "sparse attention kernel launch");
+  e = solattn::launch_sparse(d, a, s);
+  if (e != hipSuccess) return hip_status(e, "sparse attention kernel launch");
+  return hip_status(mark(3), "event record");
 }
 
 int sol_attn_fwd(const sol_shape* shape, const void* q, const void* k, const void* v, float beta,

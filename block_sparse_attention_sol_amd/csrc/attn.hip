@@ -1,27 +1,35 @@
-// attn.hip -- the fused Sol-Attn forward kernel and the dense reference kernel (gfx950).
+// attn.hip -- row statistics, the fused Sol-Attn forward kernel and the dense reference kernel
+// (gfx950).
 //
 // Method (page "Sol-Attn: Accelerating Video Generation Inference via On-the-Fly Attention
 // Sparsification", agihunt.info/papers/2607.24027): per query, a proxy score for every key block,
 // a threshold tau = mu + beta * sigma over that query's proxy row (paragraph on the per-query
-// threshold), exact attention on the kept blocks, and an approximation for the unselected blocks,
+// threshold), exact attention on the kept blocks and an approximation for the unselected blocks,
 // all inside one online-softmax pass (paragraphs on the fused operator).  Proxy and
 // approximation are fixed here as q . mean(K_blk) / sqrt(d) and one pooled token per unselected
 // block with logit s + ln(n_blk) and value mean(V_blk).
 //
-// One workgroup = 4 waves = one tile of 128 query rows of one (batch, head); each wave owns 32
-// rows, one row per lane pair (lanes c and c + 32).  Scores are computed transposed,
-// S^T = K Q^T, with Q resident in registers as the B operand, so each lane sees its own query's
-// scores.  Three sweeps:
-//   1. proxy statistics: stream the pooled keys (as three bf16 pieces hi + mid + lo, whose bf16
-//      products accumulate in fp32 to the fp32-accurate proxy) through LDS in chunks of 32 blocks;
-//      accumulate sum (s - mu)^2 with mu = q . mean_j(Kbar_j) / sqrt(d) known up front, and the
-//      largest pooled logit (an upper bound for the softmax max of the pooled tokens);
-//   2. selection + pooled tokens: recompute the same proxies, set the per-row selection bits and
-//      the tile's union of kept blocks in LDS, and fold every unselected block's pooled token into
-//      the running softmax (P.Vbar on the matrix cores, Vbar as bf16);
-//   3. exact attention: for each key block some row of the tile keeps, stage K (row-major) and V
-//      (transposed) in LDS, S^T = K Q^T, mask the rows that did not keep the block, online
-//      softmax update, O^T += V^T P^T.
+// Kernels
+//   rowstats_kernel  mu_i = q_i . g / sqrt(d) and sigma_i^2 = q_i^T C q_i / d, where g and C are the
+//                    mean and covariance of the pooled keys: the mean and population variance of
+//                    the proxy row, exactly, without visiting its M entries.  C q is one bf16
+//                    matrix product per 32 rows over the hi + mid + lo pieces of C (fp32-accurate).
+//                    Writes tau_i = mu_i + beta * sigma_i.
+//   sol_attn_kernel  one workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns
+//                    32 rows, one row per lane pair (lanes c and c + 32).  Scores are computed
+//                    transposed, S^T = K Q^T, with Q resident in registers as the B operand, so a
+//                    lane sees its own query's scores.
+//                    Sweep over the pooled keys in chunks of 32 blocks: fp32-accurate proxies from
+//                    the three bf16 pieces of Kbar, the selection bits s >= tau (per row, to the
+//                    row-mask buffer) and their union over the tile (LDS), and every unselected
+//                    block's pooled token folded into the running softmax (P Vbar on the matrix
+//                    cores, Vbar as hi + lo bf16).
+//                    Exact loop over the blocks in the union, in stages of 64 keys, double
+//                    buffered: K and V rows go straight from memory to LDS (global_load_lds), the
+//                    next stage's copy overlapping this stage's math; S^T = K Q^T, rows that did not
+//                    keep the block are masked, online softmax, O^T += V^T P^T with V^T read from
+//                    the row-major V tile by the LDS transpose read (ds_read_b64_tr_b16).
+//   dense_attn_kernel the exact loop over every key: the reference the speedup is measured against.
 // The proxy map is never written to memory; only the optional debug outputs leave the kernel.
 #include <math.h>
 
@@ -32,83 +40,88 @@ namespace solattn {
 
 namespace {
 
-constexpr int kKeyTileDense = 128;  // keys per step of the dense kernel
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kStage = 64;  // keys per pipeline stage
 
 // ---------------------------------------------------------------------------------------------
-// LDS staging
+// LDS tiles: row-major [rows][D] bf16, 16-byte chunks XOR-swizzled per row.  The swizzle makes
+// both access patterns conflict-free: 16 consecutive rows read at one logical chunk (the K / Kbar
+// A operand), and 4 consecutive rows read at two adjacent chunks (the transpose read of V).
 // ---------------------------------------------------------------------------------------------
-
-// K rows [r0, r0 + nrows) of one head -> ks (row-major, KT rows, 16-byte chunks swizzled).
-// Rows >= nrows are zero-filled.
-template <int D, int KT>
-__device__ __forceinline__ void stage_k(const uint16_t* __restrict__ kb, int64_t r0, int nrows,
-                                        u32x4* __restrict__ ks) {
-  constexpr int kChunks = D / 8;
-  constexpr int kIters = KT * kChunks / kThreads;
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int idx = it * kThreads + t;
-    const int row = idx / kChunks;
-    const int ch = idx % kChunks;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (row < nrows) val = *reinterpret_cast<const u32x4*>(kb + (r0 + row) * D + ch * 8);
-    ks[swz16<kChunks>(row, ch)] = val;
-  }
+template <int D>
+__device__ __forceinline__ int swz(int row, int ch) {
+  if constexpr (D == 128) return ch ^ (((row & 7) << 1) | ((row >> 3) & 1));
+  else return ch ^ ((((row >> 1) & 3) << 1) | ((row >> 3) & 1));
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int ch) {  // byte offset of a 16-byte chunk
+  return row * (2 * D) + (swz<D>(row, ch) << 4);
 }
 
-// V rows [r0, r0 + nrows) -> vt transposed: vt[d][key] in 8-byte slots of 4 keys, swizzled.
-// Each thread moves a 4-key x 8-dim patch.  Rows >= nrows are zero-filled.
-template <int D, int KT>
-__device__ __forceinline__ void stage_vt(const uint16_t* __restrict__ vb, int64_t r0, int nrows,
-                                         u32x2* __restrict__ vt) {
+// Copy rows [row0, row0 + ROWS) of a row-major [*, D] bf16 matrix into an LDS tile with
+// global_load_lds (16 bytes per lane, no registers).  Rows >= limit read row limit - 1 instead
+// (finite data; such keys are masked).  Every thread issues ROWS * D / 8 / kThreads loads.
+template <int D, int ROWS>
+__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ src, int64_t row0,
+                                          int64_t limit, lds_u8* tile) {
   constexpr int kChunks = D / 8;
-  constexpr int kSlots = KT / 4;
-  constexpr int kUnits = kSlots * kChunks;
-  constexpr int kIters = (kUnits + kThreads - 1) / kThreads;
+  constexpr int kIters = ROWS * kChunks / kThreads;
+  static_assert(ROWS * kChunks % kThreads == 0, "tile must split into whole wave loads");
   const int t = threadIdx.x;
+  const int wave = t >> 6;
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int idx = it * kThreads + t;
-    if (kUnits % kThreads != 0 && idx >= kUnits) break;
-    const int kg = idx / kChunks;
-    const int ch = idx % kChunks;
-    u32x4 a[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 4 * kg + e;
-      a[e] = u32x4{0u, 0u, 0u, 0u};
-      if (row < nrows) a[e] = *reinterpret_cast<const u32x4*>(vb + (r0 + row) * D + ch * 8);
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      // dims 8ch + 2m (low halves) and 8ch + 2m + 1 (high halves)
-      u32x2 lo, hi;
-      lo[0] = (a[0][m] & 0xffffu) | (a[1][m] << 16);
-      lo[1] = (a[2][m] & 0xffffu) | (a[3][m] << 16);
-      hi[0] = (a[0][m] >> 16) | (a[1][m] & 0xffff0000u);
-      hi[1] = (a[2][m] >> 16) | (a[3][m] & 0xffff0000u);
-      vt[swz8<kSlots>(8 * ch + 2 * m, kg)] = lo;
-      vt[swz8<kSlots>(8 * ch + 2 * m + 1, kg)] = hi;
-    }
+  for (int i = 0; i < kIters; ++i) {
+    const int p = i * kThreads + t;  // physical slot written by this lane
+    const int row = p / kChunks;
+    const int ch = swz<D>(row, p % kChunks);  // logical chunk stored in that slot (XOR involution)
+    int64_t grow = row0 + row;
+    if (grow >= limit) grow = limit - 1;
+    const uint16_t* g = src + grow * D + ch * 8;
+    lds_u8* dst = tile + (i * kThreads + wave * 64) * 16;  // wave-uniform; lane l lands at +16 l
+    __builtin_amdgcn_global_load_lds((const void*)g, (__attribute__((address_space(3))) void*)dst,
+                                     16, 0, 0);
   }
+}
+template <int D, int ROWS>
+constexpr int tile_loads() { return ROWS * (D / 8) / kThreads; }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads: the pipelined loops order their
+// LDS traffic themselves (explicit vmcnt waits for the LDS-bound copies; LDS reads are consumed
+// before the barrier), so the fence's wait for every outstanding load -- including the next
+// stage's prefetch -- is not wanted.  The empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void bar() {
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const lds_u8* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
 }
 
 // ---------------------------------------------------------------------------------------------
 // Per-wave tile math
 // ---------------------------------------------------------------------------------------------
 
-// S^T for 32 keys (rows kr0 .. kr0 + 31 of the staged K tile) against this lane's query.
+// S^T (32 keys = tile rows kr0 .. kr0 + 31) x (this lane's query): D/16 MFMAs.
 template <int D>
-__device__ __forceinline__ f32x16 scores32(const u32x4* __restrict__ ks, int kr0,
-                                           const bf16x8 (&qf)[D / 16]) {
-  constexpr int kChunks = D / 8;
+__device__ __forceinline__ f32x16 scores32(const lds_u8* tile, int kr0, const bf16x8 (&qf)[D / 16],
+                                           f32x16 acc) {
   const int lane = threadIdx.x & 63;
   const int c = lane & 31, h = lane >> 5;
-  f32x16 acc = {};
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    const u32x4 raw = ks[swz16<kChunks>(kr0 + c, 2 * kk + h)];
+    const u32x4 raw = lds_read16(tile + tile_off<D>(kr0 + c, 2 * kk + h));
     acc = mfma32(__builtin_bit_cast(bf16x8, raw), qf[kk], acc);
   }
   return acc;
@@ -133,24 +146,37 @@ __device__ __forceinline__ float round_p(const float* p, uint32_t* pk, float sum
   return sum;
 }
 
-// O^T[dsub] += V^T P^T for one 32-key score block kb (two 16-key steps), V^T staged in vt with
-// kSlots 8-byte slots per d row.
-template <int D, int kSlots>
-__device__ __forceinline__ void pv32(const u32x2* __restrict__ vt, int kb, const uint32_t* pk,
+// O^T[ds] += V^T P^T for one 32-key score block (tile rows kr0 .. kr0 + 31 of a V tile).
+// Score register v of lane half h belongs to key 8*(v/4) + 4*h + v%4; the probabilities of
+// registers 8*e2 .. 8*e2 + 7 form the B operand of one MFMA, whose A operand (V^T restricted to
+// those 8 keys, this lane's d column) comes from two LDS transpose reads.  In each 16-lane group
+// the source lane j points at key row (e = j/4 of the 4 keys) and 4 columns (j%4); the hardware
+// hands lane i column i of each of the 4 rows.
+template <int D>
+__device__ __forceinline__ void pv32(const lds_u8* vtile, int kr0, const uint32_t* pk,
                                      f32x16 (&o)[D / 32]) {
   const int lane = threadIdx.x & 63;
-  const int c = lane & 31, h = lane >> 5;
+  const int grp = lane >> 4, j = lane & 15;
+  const int h = grp >> 1, cg = grp & 1;
 #pragma unroll
   for (int e2 = 0; e2 < 2; ++e2) {
     const bf16x8 b = p_operand(pk, e2);
-    const int s0 = 8 * kb + 4 * e2 + h;
 #pragma unroll
     for (int ds = 0; ds < D / 32; ++ds) {
-      const int row = 32 * ds + c;
+      const int d0 = 32 * ds + 16 * cg + 4 * (j & 3);
+      s16x4 x[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int row = kr0 + 16 * e2 + 8 * r + 4 * h + (j >> 2);
+        const lds_u8* p = vtile + tile_off<D>(row, d0 >> 3) + ((d0 >> 2) & 1) * 8;
+        x[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(p));
+      }
       u32x4 raw;
-      const u32x2 x0 = vt[swz8<kSlots>(row, s0)];
-      const u32x2 x1 = vt[swz8<kSlots>(row, s0 + 2)];
-      raw[0] = x0[0]; raw[1] = x0[1]; raw[2] = x1[0]; raw[3] = x1[1];
+      raw[0] = __builtin_bit_cast(u32x2, x[0])[0];
+      raw[1] = __builtin_bit_cast(u32x2, x[0])[1];
+      raw[2] = __builtin_bit_cast(u32x2, x[1])[0];
+      raw[3] = __builtin_bit_cast(u32x2, x[1])[1];
       o[ds] = mfma32(__builtin_bit_cast(bf16x8, raw), b, o[ds]);
     }
   }
@@ -159,21 +185,21 @@ __device__ __forceinline__ void pv32(const u32x2* __restrict__ vt, int kb, const
 // Key offset (within a 32-key score block) of result register v for lane half h.
 __device__ __forceinline__ int key_of(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
 
-// One exact key tile (KT keys staged in ks / vt) folded into the running softmax of this lane.
-// `active`: this lane's row takes part (kept block, valid row); `nvalid`: keys < N in the tile.
-template <int D, int KT>
-__device__ __forceinline__ void exact_tile(const u32x4* __restrict__ ks, const u32x2* __restrict__ vt,
-                                           const bf16x8 (&qf)[D / 16], bool active, int nvalid,
-                                           float sl2, float& mrun, float& lsum,
-                                           f32x16 (&o)[D / 32]) {
-  constexpr int NS = KT / 32;
+// One 64-key stage (K and V tiles in LDS) folded into this lane's running softmax.
+// active: this row takes part; nvalid: keys of the stage below N.
+template <int D>
+__device__ __forceinline__ void exact_stage(const lds_u8* ktile, const lds_u8* vtile,
+                                            const bf16x8 (&qf)[D / 16], bool active, int nvalid,
+                                            float sl2, float& mrun, float& lsum,
+                                            f32x16 (&o)[D / 32]) {
+  constexpr int NS = kStage / 32;
   const int h = (threadIdx.x & 63) >> 5;
   f32x16 s[NS];
 #pragma unroll
-  for (int kb = 0; kb < NS; ++kb) s[kb] = scores32<D>(ks, 32 * kb, qf);
+  for (int kb = 0; kb < NS; ++kb) s[kb] = scores32<D>(ktile, 32 * kb, qf, f32x16{});
 
   float mt = -INFINITY;
-  if (nvalid >= KT) {
+  if (nvalid >= kStage) {
 #pragma unroll
     for (int kb = 0; kb < NS; ++kb)
 #pragma unroll
@@ -187,7 +213,7 @@ __device__ __forceinline__ void exact_tile(const u32x4* __restrict__ ks, const u
   }
   mt = fmaxf(mt, swap_halves(mt));
   const float mnew = active ? fmaxf(mrun, mt * sl2) : mrun;
-  const float alpha = exp2f(mrun - mnew);
+  const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
   mrun = mnew;
   uint32_t pk[NS][8];
   float ps = 0.f;
@@ -197,7 +223,7 @@ __device__ __forceinline__ void exact_tile(const u32x4* __restrict__ ks, const u
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const bool ok = active && (32 * kb + key_of(v, h) < nvalid);
-      p[v] = ok ? exp2f(fmaf(s[kb][v], sl2, -mnew)) : 0.f;
+      p[v] = ok ? __builtin_amdgcn_exp2f(fmaf(s[kb][v], sl2, -mnew)) : 0.f;
     }
     ps = round_p(p, pk[kb], ps);
   }
@@ -207,32 +233,7 @@ __device__ __forceinline__ void exact_tile(const u32x4* __restrict__ ks, const u
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[ds][v] *= alpha;
 #pragma unroll
-  for (int kb = 0; kb < NS; ++kb) pv32<D, KT / 4>(vt, kb, pk[kb], o);
-}
-
-// Write O = O^T / l for this lane's row (and its log-sum-exp if asked).
-// out_f32 (optional): the same values before rounding to bf16.
-template <int D>
-__device__ __forceinline__ void epilogue(const f32x16 (&o)[D / 32], float mrun, float lsum,
-                                         bool valid, uint16_t* __restrict__ orow, float* lse_out,
-                                         float* __restrict__ frow = nullptr) {
-  const int h = (threadIdx.x & 63) >> 5;
-  const float l = lsum + swap_halves(lsum);
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
-  if (!valid) return;
-#pragma unroll
-  for (int ds = 0; ds < D / 32; ++ds)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float x0 = o[ds][4 * g + 0] * inv, x1 = o[ds][4 * g + 1] * inv;
-      const float x2 = o[ds][4 * g + 2] * inv, x3 = o[ds][4 * g + 3] * inv;
-      u32x2 w;
-      w[0] = pack_bf16x2(x0, x1);
-      w[1] = pack_bf16x2(x2, x3);
-      *reinterpret_cast<u32x2*>(orow + 32 * ds + 8 * g + 4 * h) = w;
-      if (frow) *reinterpret_cast<f32x4*>(frow + 32 * ds + 8 * g + 4 * h) = f32x4{x0, x1, x2, x3};
-    }
-  if (lse_out && h == 0) *lse_out = l > 0.f ? (mrun + log2f(l)) * kLn2 : -INFINITY;
+  for (int kb = 0; kb < NS; ++kb) pv32<D>(vtile, 32 * kb, pk[kb], o);
 }
 
 template <int D>
@@ -247,45 +248,164 @@ __device__ __forceinline__ void load_q(const uint16_t* __restrict__ qrow, bool v
   }
 }
 
+// Write O = O^T / l for the wave's 32 rows: through LDS (row-major, swizzled) so that each global
+// store instruction writes whole rows.  stage: this wave's 32 x D bf16 LDS area.  Also the
+// optional fp32 output and log-sum-exp.  Called by every lane of the wave.
+template <int D>
+__device__ __forceinline__ void epilogue(const f32x16 (&o)[D / 32], float mrun, float lsum,
+                                         int64_t row0, int64_t N, uint16_t* __restrict__ out,
+                                         float* __restrict__ out_f32, float* __restrict__ lse,
+                                         lds_u8* stage) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 31, h = lane >> 5;
+  const int64_t row = row0 + c;
+  const float l = lsum + swap_halves(lsum);
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+  for (int ds = 0; ds < D / 32; ++ds)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float x0 = o[ds][4 * g + 0] * inv, x1 = o[ds][4 * g + 1] * inv;
+      const float x2 = o[ds][4 * g + 2] * inv, x3 = o[ds][4 * g + 3] * inv;
+      u32x2 w;
+      w[0] = pack_bf16x2(x0, x1);
+      w[1] = pack_bf16x2(x2, x3);
+      // d = 32 ds + 8 g + 4 h + (0..3): chunk 4 ds + g, half h
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+          stage + tile_off<D>(c, 4 * ds + g) + 8 * h) = w;
+      if (out_f32 && row < N)
+        *reinterpret_cast<f32x4*>(out_f32 + row * D + 32 * ds + 8 * g + 4 * h) = f32x4{x0, x1, x2, x3};
+    }
+  if (lse && h == 0 && row < N) lse[row] = l > 0.f ? (mrun + log2f(l)) * kLn2 : -INFINITY;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  constexpr int kChunks = D / 8;
+#pragma unroll
+  for (int i = 0; i < 32 * kChunks / 64; ++i) {
+    const int idx = i * 64 + lane;
+    const int r = idx / kChunks, ch = idx % kChunks;
+    const u32x4 v = lds_read16(stage + tile_off<D>(r, ch));
+    if (row0 + r < N) *reinterpret_cast<u32x4*>(out + (row0 + r) * D + ch * 8) = v;
+  }
+}
+
+// Work item of this workgroup, XCD-aware: workgroup i runs on XCD i % 8, so XCD x is given the
+// contiguous range of (head, query tile) items x*P .. x*P + P - 1 and the tiles of one head that
+// run at the same time share that XCD's L2.  Returns false for the padding workgroups.
+__device__ __forceinline__ bool work_item(int64_t total, int64_t& w) {
+  const int64_t per = (total + 7) / 8;
+  w = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  return w < total;
+}
+
 }  // namespace
+
+// ---------------------------------------------------------------------------------------------
+// Row statistics: mu, sigma, tau of every query's proxy row
+// ---------------------------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void rowstats_kernel(RowStatsArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  lds_u8* smem = (lds_u8*)smem_raw;
+  constexpr int kTilesPerWg = 4;
+  const int64_t ntiles = (a.N + kQTile - 1) / kQTile;
+  const int64_t groups = (ntiles + kTilesPerWg - 1) / kTilesPerWg;
+  const int64_t bh = blockIdx.x / groups;
+  const int64_t grp = blockIdx.x % groups;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane & 31, h = lane >> 5;
+
+  // C pieces -> LDS, smallest first: tile p holds piece lo (p = 0), mid (1), hi (2)
+  const uint16_t* cbase = a.cp + bh * D * D;
+  const int64_t piece = a.BH * D * D;
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+    load_tile<D, D>(cbase + (2 - p) * piece, 0, D, smem + p * D * D * 2);
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+  const float* kg = a.kglob + bh * D;
+  for (int tt = 0; tt < kTilesPerWg; ++tt) {
+    const int64_t tile = grp * kTilesPerWg + tt;
+    if (tile >= ntiles) break;
+    const int64_t row = tile * kQTile + wave * 32 + c;
+    const bool valid = row < a.N;
+    const uint16_t* qrow = a.q + (bh * a.N + row) * D;
+    bf16x8 qf[D / 16];
+    load_q<D>(qrow, valid, qf);
+    float mpart = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mpart = fmaf((float)qf[kk][e], kg[16 * kk + 8 * h + e], mpart);
+    float vpart = 0.f;
+#pragma unroll
+    for (int ab = 0; ab < D / 32; ++ab) {
+      f32x16 y = {};
+#pragma unroll
+      for (int p = 0; p < 3; ++p) y = scores32<D>(smem + p * D * D * 2, 32 * ab, qf, y);
+      // y[v] = (C q)[a], a = 32 ab + 8 (v/4) + 4 h + v%4
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 qq = {0u, 0u};
+        if (valid) qq = *reinterpret_cast<const u32x2*>(qrow + 32 * ab + 8 * g + 4 * h);
+        vpart = fmaf(y[4 * g + 0], bf16_lo(qq[0]), vpart);
+        vpart = fmaf(y[4 * g + 1], bf16_hi(qq[0]), vpart);
+        vpart = fmaf(y[4 * g + 2], bf16_lo(qq[1]), vpart);
+        vpart = fmaf(y[4 * g + 3], bf16_hi(qq[1]), vpart);
+      }
+    }
+    const float mu = (mpart + swap_halves(mpart)) * inv_sqrt_d;
+    const float var = (vpart + swap_halves(vpart)) / (float)D;
+    const float sigma = sqrtf(fmaxf(var, 0.f));
+    const float tau = isinf(a.beta) ? a.beta : fmaf(a.beta, sigma, mu);
+    if (valid && h == 0) {
+      a.tau[bh * a.N + row] = tau;
+      if (a.mu) a.mu[bh * a.N + row] = mu;
+      if (a.sigma) a.sigma[bh * a.N + row] = sigma;
+      if (a.tau_out) a.tau_out[bh * a.N + row] = tau;
+    }
+  }
+}
 
 // ---------------------------------------------------------------------------------------------
 // Fused Sol-Attn kernel
 // ---------------------------------------------------------------------------------------------
 
 template <int D, int BLK>
-__global__ __launch_bounds__(kThreads) void sol_attn_kernel(SparseArgs a) {
-  constexpr int kChunks = D / 8;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  // region A: sweeps 1-2 (pooled chunk) or sweep 3 (K and V^T tiles)
-  constexpr int kTileBytes = BLK * D * 2;
-  constexpr int kChunkBytes = 3 * 32 * D * 2 + 2 * D * 32 * 2;
-  constexpr int kRegionA = 2 * kTileBytes > kChunkBytes ? 2 * kTileBytes : kChunkBytes;
+__global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  lds_u8* smem = (lds_u8*)smem_raw;
+  constexpr int kTileBytes = kStage * D * 2;          // one 64-row tile
+  constexpr int kStageBytes = 2 * kTileBytes;         // K + V
+  constexpr int kChunkTile = 32 * D * 2;              // one 32-row pooled tile
+  constexpr int kRegionA = 2 * kStageBytes > 5 * kChunkTile ? 2 * kStageBytes : 5 * kChunkTile;
+  constexpr int kStagesPerBlock = BLK / kStage;
+  constexpr int kLoadsPerStage = 2 * tile_loads<D, kStage>();
+  uint32_t* umask = (uint32_t*)(smem_raw + kRegionA);
   const int W = (int)(a.Mp / 32);
-  u32x4* ks = reinterpret_cast<u32x4*>(smem);
-  u32x2* vt = reinterpret_cast<u32x2*>(smem + kTileBytes);
-  u32x4* kpc = reinterpret_cast<u32x4*>(smem);                       // [3][32][D]
-  u32x2* vbc = reinterpret_cast<u32x2*>(smem + 3 * 32 * D * 2);      // [D][32]
-  uint32_t* rowmask = reinterpret_cast<uint32_t*>(smem + kRegionA);  // [128][W]
-  uint32_t* umask = rowmask + kQTile * W;                            // [W]
-  int* klist = reinterpret_cast<int*>(umask + W);                    // [Mp]
-  int* nkept_s = klist + a.Mp;
 
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, c = lane & 31, h = lane >> 5;
   const int64_t ntiles = (a.N + kQTile - 1) / kQTile;
-  const int64_t bh = blockIdx.x / ntiles;
-  const int64_t tile = blockIdx.x % ntiles;
-  const int rloc = wave * 32 + c;                 // row within the tile
-  const int64_t row = tile * kQTile + rloc;
+  int64_t w;
+  if (!work_item(a.BH * ntiles, w)) return;
+  const int64_t bh = w / ntiles;
+  const int64_t tile = w % ntiles;
+  const int64_t row0 = tile * kQTile + wave * 32;   // first row of this wave
+  const int64_t row = row0 + c;
   const bool rvalid = row < a.N;
 
   const uint16_t* qb = a.q + bh * a.N * D;
   const uint16_t* kb = a.k + bh * a.N * D;
   const uint16_t* vb = a.v + bh * a.N * D;
+  uint32_t* rmask = a.rowmask + (bh * a.N) * W;
 
   bf16x8 qf[D / 16];
   load_q<D>(qb + row * D, rvalid, qf);
+  const float tau = rvalid ? a.tau[bh * a.N + row] : INFINITY;  // padding rows keep nothing
 
   const float inv_sqrt_d = 1.0f / sqrtf((float)D);
   const float sl2 = inv_sqrt_d * kLog2e;
@@ -293,101 +413,36 @@ __global__ __launch_bounds__(kThreads) void sol_attn_kernel(SparseArgs a) {
   const float l2n_full = log2f((float)a.block);
   const float l2n_last = log2f((float)n_last);
 
-  // mu = q . kglob / sqrt(d): each lane half holds half of the head dimension.
-  float mu;
-  {
-    const float* kg = a.kglob + bh * D;
-    float part = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) part = fmaf((float)qf[kk][e], kg[16 * kk + 8 * h + e], part);
-    mu = (part + swap_halves(part)) * inv_sqrt_d;
-  }
+  for (int i = t; i < W; i += kThreads) umask[i] = 0u;
 
-  for (int w = t; w < W; w += kThreads) umask[w] = 0u;
-
-  const int64_t nchunks = a.Mp / 32;
-  const uint16_t* kp_hi = a.kp + ((0 * a.BH + bh) * a.Mp) * D;
-  const uint16_t* kp_mid = a.kp + ((1 * a.BH + bh) * a.Mp) * D;
-  const uint16_t* kp_lo = a.kp + ((2 * a.BH + bh) * a.Mp) * D;
-  const uint16_t* vbt = a.vbt + bh * D * a.Mp;                  // Vbar^T, hi piece
-  const uint16_t* vbt_lo = a.vbt + (a.BH + bh) * D * a.Mp;       // Vbar^T, lo piece
-
-  auto stage_chunk = [&](int64_t cb, bool with_v) {
-    constexpr int kPieceUnits = 32 * kChunks;
-    for (int idx = t; idx < 3 * kPieceUnits; idx += kThreads) {
-      const int p = idx / kPieceUnits;
-      const int r = (idx % kPieceUnits) / kChunks;
-      const int ch = idx % kChunks;
-      const uint16_t* src = (p == 0 ? kp_lo : (p == 1 ? kp_mid : kp_hi)) + (cb * 32 + r) * D + ch * 8;
-      kpc[p * 32 * kChunks + swz16<kChunks>(r, ch)] = *reinterpret_cast<const u32x4*>(src);
-    }
-    if (with_v) {
-      // Vbar^T chunk, lo and hi pieces: D rows x 32 blocks = 8 slots of 4 blocks per row
-      // (swizzled by row & 7)
-      for (int idx = t; idx < 2 * D * 8; idx += kThreads) {
-        const int piece = idx / (D * 8);
-        const int r = (idx / 8) % D, sl = idx % 8;
-        const uint16_t* src = (piece == 0 ? vbt_lo : vbt) + r * a.Mp + cb * 32 + sl * 4;
-        vbc[piece * D * 8 + r * 8 + (sl ^ (r & 7))] = *reinterpret_cast<const u32x2*>(src);
-      }
-    }
-  };
-  // fp32-accurate proxies (raw dot products, not yet scaled) of this lane's query for the 32
-  // blocks of the staged chunk: pieces accumulated smallest first.
-  auto chunk_scores = [&]() {
-    f32x16 acc = {};
-#pragma unroll
-    for (int p = 0; p < 3; ++p)
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const u32x4 raw = kpc[p * 32 * kChunks + swz16<kChunks>(c, 2 * kk + h)];
-        acc = mfma32(__builtin_bit_cast(bf16x8, raw), qf[kk], acc);
-      }
-    return acc;
-  };
-
-  // ---- sweep 1: sigma and the pooled-logit bound ----
-  float ssq = 0.f;
-  float pmax = -INFINITY;  // log2-domain pooled logit bound
-  for (int64_t cb = 0; cb < nchunks; ++cb) {
-    __syncthreads();
-    stage_chunk(cb, false);
-    __syncthreads();
-    const f32x16 acc = chunk_scores();
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t j = cb * 32 + key_of(v, h);
-      if (j < a.M) {
-        const float s = acc[v] * inv_sqrt_d;
-        const float dl = s - mu;
-        ssq = fmaf(dl, dl, ssq);
-        pmax = fmaxf(pmax, fmaf(acc[v], sl2, j == a.M - 1 ? l2n_last : l2n_full));
-      }
-    }
-  }
-  ssq += swap_halves(ssq);
-  pmax = fmaxf(pmax, swap_halves(pmax));
-  const float sigma = sqrtf(ssq / (float)a.M);
-  float tau;
-  if (isinf(a.beta)) tau = a.beta;
-  else tau = fmaf(a.beta, sigma, mu);
-  if (!rvalid) tau = INFINITY;  // padding rows keep nothing
-
-  // ---- sweep 2: selection bits, tile union, pooled tokens ----
+  // ---- pooled sweep: selection bits, tile union, pooled tokens ----
+  const int64_t piece = a.BH * a.Mp * D;
+  const uint16_t* kp0 = a.kp + bh * a.Mp * D;  // hi; mid at + piece, lo at + 2 piece
+  const uint16_t* vp0 = a.vbp + bh * a.Mp * D; // hi; lo at + piece
   f32x16 o[D / 32];
 #pragma unroll
   for (int ds = 0; ds < D / 32; ++ds) o[ds] = f32x16{};
-  float mrun = a.drop ? -1e30f : pmax;
+  float mrun = -1e30f;  // running max, log2 domain
   float lsum = 0.f;
+  const int64_t nchunks = a.Mp / 32;
   for (int64_t cb = 0; cb < nchunks; ++cb) {
     __syncthreads();
-    stage_chunk(cb, !a.drop);
+    // pooled tiles: 0 lo, 1 mid, 2 hi pieces of Kbar; 3 Vbar hi, 4 Vbar lo
+    load_tile<D, 32>(kp0 + 2 * piece, cb * 32, a.Mp, smem + 0 * kChunkTile);
+    load_tile<D, 32>(kp0 + 1 * piece, cb * 32, a.Mp, smem + 1 * kChunkTile);
+    load_tile<D, 32>(kp0, cb * 32, a.Mp, smem + 2 * kChunkTile);
+    if (!a.drop) {
+      load_tile<D, 32>(vp0, cb * 32, a.Mp, smem + 3 * kChunkTile);
+      load_tile<D, 32>(vp0 + piece, cb * 32, a.Mp, smem + 4 * kChunkTile);
+    }
+    wait_vmcnt<0>();
     __syncthreads();
-    const f32x16 acc = chunk_scores();
+    f32x16 acc = {};
+#pragma unroll
+    for (int p = 0; p < 3; ++p) acc = scores32<D>(smem + p * kChunkTile, 0, qf, acc);
     uint32_t bits = 0u;
-    float p[16];
+    float x[16];
+    float cmax = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int kj = key_of(v, h);
@@ -395,153 +450,198 @@ __global__ __launch_bounds__(kThreads) void sol_attn_kernel(SparseArgs a) {
       const bool valid = j < a.M;
       const bool sel = valid && (acc[v] * inv_sqrt_d >= tau);
       bits |= (sel ? 1u : 0u) << kj;
-      p[v] = (valid && !sel && !a.drop)
-                 ? exp2f(fmaf(acc[v], sl2, (j == a.M - 1 ? l2n_last : l2n_full) - mrun))
-                 : 0.f;
+      x[v] = (valid && !sel) ? fmaf(acc[v], sl2, j == a.M - 1 ? l2n_last : l2n_full) : -INFINITY;
+      cmax = fmaxf(cmax, x[v]);
     }
     const uint32_t word = bits | swap_halves_u(bits);
-    if (h == 0) rowmask[rloc * W + cb] = word;
-    if (h == 0 && a.mask && rvalid) a.mask[(bh * a.N + row) * W + cb] = word;
+    if (h == 0 && rvalid) rmask[row * W + cb] = word;
     uint32_t u = word;
 #pragma unroll
     for (int off = 16; off >= 1; off >>= 1) u |= (uint32_t)__shfl_xor((int)u, off, kWave);
     if (lane == 0 && u) atomicOr(&umask[cb], u);
     if (!a.drop) {
+      cmax = fmaxf(cmax, swap_halves(cmax));
+      const float mnew = fmaxf(mrun, cmax);
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+      mrun = mnew;
+      float p[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(x[v] - mnew);
       uint32_t pk[8];
-      lsum = round_p(p, pk, lsum);
+      lsum = round_p(p, pk, lsum * alpha);
 #pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) {
-        const bf16x8 bop = p_operand(pk, e2);
+      for (int ds = 0; ds < D / 32; ++ds)
 #pragma unroll
-        for (int piece = 0; piece < 2; ++piece)  // Vbar lo, then hi
-#pragma unroll
-          for (int ds = 0; ds < D / 32; ++ds) {
-            const int r = 32 * ds + c;
-            const int s0 = 4 * e2 + h;
-            const u32x2* vp = vbc + piece * D * 8;
-            const u32x2 x0 = vp[r * 8 + (s0 ^ (r & 7))];
-            const u32x2 x1 = vp[r * 8 + ((s0 + 2) ^ (r & 7))];
-            u32x4 raw;
-            raw[0] = x0[0]; raw[1] = x0[1]; raw[2] = x1[0]; raw[3] = x1[1];
-            o[ds] = mfma32(__builtin_bit_cast(bf16x8, raw), bop, o[ds]);
-          }
+        for (int v = 0; v < 16; ++v) o[ds][v] *= alpha;
+      pv32<D>(smem + 4 * kChunkTile, 0, pk, o);  // Vbar lo
+      pv32<D>(smem + 3 * kChunkTile, 0, pk, o);  // Vbar hi
+    }
+  }
+  __syncthreads();
+
+  // ---- exact attention over the kept blocks, double-buffered 64-key stages ----
+  // Stage iterator: blocks j in the tile's union (ascending), stages s of each block with keys
+  // below N.  All values are wave-uniform.
+  int it_w = -1;
+  uint32_t it_u = 0u;
+  int it_j = -1, it_s = kStagesPerBlock;
+  auto next_stage = [&](int& j, int& s) -> bool {
+    for (;;) {
+      if (it_j >= 0 && it_s + 1 < kStagesPerBlock &&
+          (int64_t)it_j * BLK + (int64_t)(it_s + 1) * kStage < a.N) {
+        ++it_s;
+        j = it_j;
+        s = it_s;
+        return true;
       }
+      while (it_u == 0u) {
+        if (++it_w >= W) return false;
+        it_u = __builtin_amdgcn_readfirstlane(umask[it_w]);
+      }
+      const int b = __builtin_ctz(it_u);
+      it_u &= it_u - 1u;
+      it_j = it_w * 32 + b;
+      it_s = -1;
     }
-  }
-  __syncthreads();
+  };
+  auto issue = [&](int j, int s, int buf) {
+    const int64_t r0 = (int64_t)j * BLK + (int64_t)s * kStage;
+    lds_u8* base = smem + buf * kStageBytes;
+    load_tile<D, kStage>(kb, r0, a.N, base);
+    load_tile<D, kStage>(vb, r0, a.N, base + kTileBytes);
+  };
 
-  // ---- kept-block list of the tile ----
-  // each of the first W threads expands one union word at its prefix offset
-  for (int w = t; w < W; w += kThreads) {
-    int off = 0;
-    for (int w2 = 0; w2 < w; ++w2) off += __builtin_popcount(umask[w2]);
-    uint32_t u = umask[w];
-    while (u) {
-      const int b = __builtin_ctz(u);
-      u &= u - 1u;
-      klist[off++] = w * 32 + b;
+  int kept_blocks = 0;
+  int cur_j = -1, cur_s = 0;
+  bool have = next_stage(cur_j, cur_s);
+  if (have) issue(cur_j, cur_s, 0);
+  int buf = 0;
+  int mask_w = -1;
+  uint32_t mask_word = 0u;
+  while (have) {
+    int nj = -1, ns = 0;
+    const bool more = next_stage(nj, ns);
+    if (more) {
+      issue(nj, ns, buf ^ 1);
+      wait_vmcnt<kLoadsPerStage>();
+    } else {
+      wait_vmcnt<0>();
     }
-    if (w == W - 1) {
-      *nkept_s = off;
-      if (a.tile_kept) a.tile_kept[bh * ntiles + tile] = off;
+    bar();
+    if (cur_s == 0) ++kept_blocks;
+    if ((cur_j >> 5) != mask_w) {
+      mask_w = cur_j >> 5;
+      mask_word = rvalid ? rmask[row * W + mask_w] : 0u;
     }
+    const bool active = (mask_word >> (cur_j & 31)) & 1u;
+    const int64_t r0 = (int64_t)cur_j * BLK + (int64_t)cur_s * kStage;
+    const int nvalid = (int)((a.N - r0) < kStage ? (a.N - r0) : kStage);
+    const lds_u8* base = smem + buf * kStageBytes;
+    exact_stage<D>(base, base + kTileBytes, qf, active, nvalid, sl2, mrun, lsum, o);
+    bar();
+    buf ^= 1;
+    cur_j = nj;
+    cur_s = ns;
+    have = more;
   }
-  __syncthreads();
-  const int nkept = *nkept_s;
+  if (a.tile_kept && t == 0) a.tile_kept[bh * ntiles + tile] = kept_blocks;
 
-  // ---- sweep 3: exact attention over the kept blocks ----
-  for (int idx = 0; idx < nkept; ++idx) {
-    const int j = klist[idx];
-    const int64_t r0 = (int64_t)j * BLK;
-    const int nrows = (int)((a.N - r0) < BLK ? (a.N - r0) : BLK);
-    __syncthreads();
-    stage_k<D, BLK>(kb, r0, nrows, ks);
-    stage_vt<D, BLK>(vb, r0, nrows, vt);
-    __syncthreads();
-    const bool active = rvalid && ((rowmask[rloc * W + (j >> 5)] >> (j & 31)) & 1u);
-    exact_tile<D, BLK>(ks, vt, qf, active, nrows, sl2, mrun, lsum, o);
-  }
-
-  epilogue<D>(o, mrun, lsum, rvalid, a.out + (bh * a.N + row) * D,
-              a.lse ? a.lse + bh * a.N + row : nullptr,
-              a.out_f32 ? a.out_f32 + (bh * a.N + row) * D : nullptr);
-  if (h == 0 && rvalid) {
-    if (a.mu) a.mu[bh * a.N + row] = mu;
-    if (a.sigma) a.sigma[bh * a.N + row] = sigma;
-    if (a.tau) a.tau[bh * a.N + row] = tau;
-  }
+  epilogue<D>(o, mrun, lsum, row0, a.N, a.out + bh * a.N * D,
+              a.out_f32 ? a.out_f32 + bh * a.N * D : nullptr, a.lse ? a.lse + bh * a.N : nullptr,
+              smem + wave * 32 * D * 2);
 }
 
 // ---------------------------------------------------------------------------------------------
-// Dense reference kernel: same tile machinery, every key, no routing.
+// Dense reference kernel: the exact loop over every key, no routing.
 // ---------------------------------------------------------------------------------------------
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void dense_attn_kernel(const uint16_t* __restrict__ q,
-                                                              const uint16_t* __restrict__ k,
-                                                              const uint16_t* __restrict__ v,
-                                                              uint16_t* __restrict__ out,
-                                                              float* __restrict__ lse, int64_t N) {
-  constexpr int KT = kKeyTileDense;
-  constexpr int kTileBytes = KT * D * 2;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  u32x4* ks = reinterpret_cast<u32x4*>(smem);
-  u32x2* vt = reinterpret_cast<u32x2*>(smem + kTileBytes);
-
+__global__ __launch_bounds__(kThreads, 2) void dense_attn_kernel(const uint16_t* __restrict__ q,
+                                                                 const uint16_t* __restrict__ k,
+                                                                 const uint16_t* __restrict__ v,
+                                                                 uint16_t* __restrict__ out,
+                                                                 float* __restrict__ lse,
+                                                                 int64_t BH, int64_t N) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  lds_u8* smem = (lds_u8*)smem_raw;
+  constexpr int kTileBytes = kStage * D * 2;
+  constexpr int kStageBytes = 2 * kTileBytes;
+  constexpr int kLoadsPerStage = 2 * tile_loads<D, kStage>();
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, c = lane & 31;
   const int64_t ntiles = (N + kQTile - 1) / kQTile;
-  const int64_t bh = blockIdx.x / ntiles;
-  const int64_t tile = blockIdx.x % ntiles;
-  const int64_t row = tile * kQTile + wave * 32 + c;
+  int64_t w;
+  if (!work_item(BH * ntiles, w)) return;
+  const int64_t bh = w / ntiles;
+  const int64_t tile = w % ntiles;
+  const int64_t row0 = tile * kQTile + wave * 32;
+  const int64_t row = row0 + c;
   const bool rvalid = row < N;
+  const uint16_t* kb = k + bh * N * D;
+  const uint16_t* vb = v + bh * N * D;
 
   bf16x8 qf[D / 16];
   load_q<D>(q + (bh * N + row) * D, rvalid, qf);
   const float sl2 = kLog2e / sqrtf((float)D);
-
   f32x16 o[D / 32];
 #pragma unroll
   for (int ds = 0; ds < D / 32; ++ds) o[ds] = f32x16{};
   float mrun = -1e30f, lsum = 0.f;
-  const uint16_t* kb = k + bh * N * D;
-  const uint16_t* vb = v + bh * N * D;
-  for (int64_t r0 = 0; r0 < N; r0 += KT) {
-    const int nrows = (int)((N - r0) < KT ? (N - r0) : KT);
-    __syncthreads();
-    stage_k<D, KT>(kb, r0, nrows, ks);
-    stage_vt<D, KT>(vb, r0, nrows, vt);
-    __syncthreads();
-    exact_tile<D, KT>(ks, vt, qf, true, nrows, sl2, mrun, lsum, o);
+
+  const int64_t nst = (N + kStage - 1) / kStage;
+  load_tile<D, kStage>(kb, 0, N, smem);
+  load_tile<D, kStage>(vb, 0, N, smem + kTileBytes);
+  int buf = 0;
+  for (int64_t st = 0; st < nst; ++st) {
+    if (st + 1 < nst) {
+      lds_u8* nbase = smem + (buf ^ 1) * kStageBytes;
+      load_tile<D, kStage>(kb, (st + 1) * kStage, N, nbase);
+      load_tile<D, kStage>(vb, (st + 1) * kStage, N, nbase + kTileBytes);
+      wait_vmcnt<kLoadsPerStage>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    bar();
+    const int64_t r0 = st * kStage;
+    const int nvalid = (int)((N - r0) < kStage ? (N - r0) : kStage);
+    const lds_u8* base = smem + buf * kStageBytes;
+    exact_stage<D>(base, base + kTileBytes, qf, true, nvalid, sl2, mrun, lsum, o);
+    bar();
+    buf ^= 1;
   }
-  epilogue<D>(o, mrun, lsum, rvalid, out + (bh * N + row) * D, lse ? lse + bh * N + row : nullptr);
+  epilogue<D>(o, mrun, lsum, row0, N, out + bh * N * D, nullptr, lse ? lse + bh * N : nullptr,
+              smem + wave * 32 * D * 2);
 }
 
 // ---------------------------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------------------------
 
-static size_t sparse_smem_bytes(int d, int block, int64_t Mp) {
-  const size_t tile = (size_t)block * d * 2;
-  const size_t chunk = (size_t)3 * 32 * d * 2 + (size_t)2 * d * 32 * 2;
-  const size_t regionA = 2 * tile > chunk ? 2 * tile : chunk;
-  const size_t W = (size_t)(Mp / 32);
-  return regionA + (size_t)kQTile * W * 4 + W * 4 + (size_t)Mp * 4 + 16;
+static size_t sparse_smem_bytes(int d, int64_t Mp) {
+  const size_t stage = (size_t)2 * kStage * d * 2;
+  const size_t chunk = (size_t)5 * 32 * d * 2;
+  const size_t regionA = 2 * stage > chunk ? 2 * stage : chunk;
+  return regionA + (size_t)(Mp / 32) * 4;
 }
+
+template <typename K>
+static hipError_t set_smem(K kern, size_t bytes) {
+  return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)bytes);
+}
+
+static unsigned xcd_grid(int64_t total) { return (unsigned)(((total + 7) / 8) * 8); }
 
 template <int D, int BLK>
 static hipError_t launch_sparse_t(const SparseArgs& a, hipStream_t stream) {
-  const size_t smem = sparse_smem_bytes(D, BLK, a.Mp);
+  const size_t smem = sparse_smem_bytes(D, a.Mp);
   auto kern = sol_attn_kernel<D, BLK>;
-  hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)smem);
+  hipError_t err = set_smem(kern, smem);
   if (err != hipSuccess) return err;
   const int64_t ntiles = (a.N + kQTile - 1) / kQTile;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(a.BH * ntiles)), dim3(kThreads), smem, stream, a);
+  hipLaunchKernelGGL(kern, dim3(xcd_grid(a.BH * ntiles)), dim3(kThreads), smem, stream, a);
   return hipGetLastError();
 }
-
-size_t sparse_lds_bytes(int d, int block, int64_t Mp) { return sparse_smem_bytes(d, block, Mp); }
 
 hipError_t launch_sparse(int d, const SparseArgs& a, hipStream_t stream) {
   if (d == 64 && a.block == 64) return launch_sparse_t<64, 64>(a, stream);
@@ -550,26 +650,40 @@ hipError_t launch_sparse(int d, const SparseArgs& a, hipStream_t stream) {
   return launch_sparse_t<128, 128>(a, stream);
 }
 
+template <int D>
+static hipError_t launch_rowstats_t(const RowStatsArgs& a, hipStream_t stream) {
+  const size_t smem = (size_t)3 * D * D * 2;
+  auto kern = rowstats_kernel<D>;
+  hipError_t err = set_smem(kern, smem);
+  if (err != hipSuccess) return err;
+  const int64_t ntiles = (a.N + kQTile - 1) / kQTile;
+  const int64_t groups = (ntiles + 3) / 4;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(a.BH * groups)), dim3(kThreads), smem, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowstats(int d, const RowStatsArgs& a, hipStream_t stream) {
+  return d == 64 ? launch_rowstats_t<64>(a, stream) : launch_rowstats_t<128>(a, stream);
+}
+
+template <int D>
+static hipError_t launch_dense_t(int64_t BH, int64_t N, const void* q, const void* k,
+                                 const void* v, void* out, float* lse, hipStream_t stream) {
+  const size_t smem = (size_t)4 * kStage * D * 2;
+  auto kern = dense_attn_kernel<D>;
+  hipError_t err = set_smem(kern, smem);
+  if (err != hipSuccess) return err;
+  const int64_t ntiles = (N + kQTile - 1) / kQTile;
+  hipLaunchKernelGGL(kern, dim3(xcd_grid(BH * ntiles)), dim3(kThreads), smem, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)out,
+                     lse, BH, N);
+  return hipGetLastError();
+}
+
 hipError_t launch_dense(int d, int64_t BH, int64_t N, const void* q, const void* k, const void* v,
                         void* out, float* lse, hipStream_t stream) {
-  const int64_t ntiles = (N + kQTile - 1) / kQTile;
-  const dim3 grid((unsigned)(BH * ntiles));
-  if (d == 64) {
-    const size_t smem = 2 * kKeyTileDense * 64 * 2;
-    hipError_t err = hipFuncSetAttribute((const void*)dense_attn_kernel<64>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(dense_attn_kernel<64>, grid, dim3(kThreads), smem, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)out, lse, N);
-  } else {
-    const size_t smem = 2 * kKeyTileDense * 128 * 2;
-    hipError_t err = hipFuncSetAttribute((const void*)dense_attn_kernel<128>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(dense_attn_kernel<128>, grid, dim3(kThreads), smem, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)out, lse, N);
-  }
-  return hipGetLastError();
+  return d == 64 ? launch_dense_t<64>(BH, N, q, k, v, out, lse, stream)
+                 : launch_dense_t<128>(BH, N, q, k, v, out, lse, stream);
 }
 
 }  // namespace solattn

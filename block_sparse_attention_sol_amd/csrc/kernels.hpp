@@ -6,31 +6,41 @@
 
 namespace solattn {
 
-// Pooled K/V of every key block.  kp / vbt (and Mp) only for the attention workspace; NULL in
+// Pooled K/V of every key block.  kp / vbp (and Mp) only for the attention workspace; NULL in
 // the public pooling call.
 hipError_t launch_pool(int d, int64_t BH, int64_t N, int block, const void* k, const void* v,
-                       float* kbar, float* vbar, uint16_t* kp, uint16_t* vbt, int64_t Mp,
+                       float* kbar, float* vbar, uint16_t* kp, uint16_t* vbp, int64_t Mp,
                        hipStream_t stream);
-hipError_t launch_kglob(int d, int64_t BH, int64_t M, const float* kbar, float* kglob,
-                        hipStream_t stream);
+// Mean (fp32 and fp64) and covariance (three bf16 pieces) of the pooled keys of every head.
+hipError_t launch_kstats(int d, int64_t BH, int64_t M, const float* kbar, float* kglob,
+                         double* kglob64, uint16_t* cp, hipStream_t stream);
+
+struct RowStatsArgs {
+  const uint16_t* q;
+  const uint16_t* cp;     // [3][BH][d][d] covariance pieces (hi, mid, lo)
+  const float* kglob;     // [BH][d]
+  int64_t BH, N;
+  float beta;
+  float* tau;             // [BH][N] (workspace)
+  float* mu;              // optional outputs
+  float* sigma;
+  float* tau_out;
+};
+hipError_t launch_rowstats(int d, const RowStatsArgs& a, hipStream_t stream);
 
 struct SparseArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* out;
-  const uint16_t* kp;   // [3][BH][Mp][d]
-  const uint16_t* vbt;  // [2][BH][d][Mp] (hi, lo)
-  const float* kglob;   // [BH][d]
+  const uint16_t* kp;   // [3][BH][Mp][d] pooled keys (hi, mid, lo)
+  const uint16_t* vbp;  // [2][BH][Mp][d] pooled values (hi, lo)
+  const float* tau;     // [BH][N]
+  uint32_t* rowmask;    // [BH][N][Mp/32] selection words (written, then read back per row)
   int64_t BH, N, M, Mp;
   int block;
-  float beta;
   int drop;
   // optional outputs
-  uint32_t* mask;
-  float* mu;
-  float* sigma;
-  float* tau;
   float* lse;
   int32_t* tile_kept;
   float* out_f32;

@@ -41,7 +41,8 @@ class SolShape(ctypes.Structure):
 class SolAttnDebug(ctypes.Structure):
     _fields_ = [("mask", ctypes.c_void_p), ("mu", ctypes.c_void_p), ("sigma", ctypes.c_void_p),
                 ("tau", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("tile_kept", ctypes.c_void_p),
-                ("out_f32", ctypes.c_void_p), ("drop_unselected", ctypes.c_int)]
+                ("out_f32", ctypes.c_void_p), ("drop_unselected", ctypes.c_int),
+                ("events", ctypes.c_void_p * 4)]
 
 
 class SolError(RuntimeError):
@@ -60,6 +61,9 @@ def load_library(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} not found: build it with `python -m block_sparse_attention_sol_amd.build`")
+    # torch first: its bundled HIP runtime carries the same soname, so the library binds to the
+    # runtime (and streams) torch uses instead of loading a second copy.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     vp, sz, ci, cf = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_float
     shp = ctypes.POINTER(SolShape)
@@ -141,8 +145,9 @@ def pool_kv(k, v, block: int, stream=None):
 
 
 def attn_fwd(q, k, v, beta: float, block: int, out=None, workspace=None, debug: bool = False,
-             drop_unselected: bool = False, stream=None):
-    """Sol-Attn forward.  Returns out, or (out, dict of debug outputs) when debug/drop is set."""
+             drop_unselected: bool = False, events=None, stream=None):
+    """Sol-Attn forward.  Returns out, or (out, dict of debug outputs) when debug/drop/events is
+    set.  events: 4 raw hipEvent_t handles recorded at the kernel boundaries (see HipEvents)."""
     import torch
     lib = load_library()
     B, H, N, d = q.shape
@@ -156,7 +161,7 @@ def attn_fwd(q, k, v, beta: float, block: int, out=None, workspace=None, debug: 
     if workspace is None:
         workspace = new_workspace(q.shape, block, q.device)
     shp = _shape(q)
-    if not debug and not drop_unselected:
+    if not debug and not drop_unselected and events is None:
         _check(lib.sol_attn_fwd(ctypes.byref(shp), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
                                 float(beta), block, _dev(out, "out"), _dev(workspace, "workspace"),
                                 workspace.numel(), _stream(stream)))
@@ -180,6 +185,9 @@ def attn_fwd(q, k, v, beta: float, block: int, out=None, workspace=None, debug: 
         for key, t in dbg.items():
             setattr(dstruct, key, t.data_ptr())
     dstruct.drop_unselected = int(bool(drop_unselected))
+    if events is not None:
+        for i, e in enumerate(events):
+            dstruct.events[i] = e
     _check(lib.sol_attn_fwd_ex(ctypes.byref(shp), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
                                float(beta), block, _dev(out, "out"), _dev(workspace, "workspace"),
                                workspace.numel(), ctypes.byref(dstruct), _stream(stream)))
@@ -223,3 +231,38 @@ def kept_block_flops(tile_kept, mask, N: int, d: int, block: int) -> float:
 
 def dense_flops(B: int, H: int, N: int, d: int) -> float:
     return 4.0 * B * H * N * N * d
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch uses (for the library's timing hook)."""
+
+    def __init__(self, n: int):
+        import torch  # noqa: F401  (binds the runtime torch loaded)
+        self._hip = ctypes.CDLL("libamdhip64.so.7")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                  ctypes.c_void_p]
+        self._hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.handles = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles.append(h.value)
+
+    def record(self, i: int, stream=None):
+        if self._hip.hipEventRecord(self.handles[i], _stream(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        self._hip.hipEventSynchronize(self.handles[b])
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.handles[a], self.handles[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def __del__(self):
+        for h in getattr(self, "handles", []):
+            self._hip.hipEventDestroy(h)

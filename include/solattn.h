@@ -22,7 +22,7 @@
  *   Layout    q, k, v, out: contiguous [B][H][N][d] bf16 (raw uint16 bit patterns), device memory.
  *   Blocks    key block j covers tokens [j*block, min((j+1)*block, N)); M = ceil(N / block).
  *   Scale     1/sqrt(d), fixed.
- *   Supported d in {64, 128}; block in {64, 128}; 1 <= N <= 2^30; B*H >= 1.
+ *   Supported d in {64, 128}; block in {64, 128}; 1 <= N <= 2^22; 1 <= B*H <= 65535.
  *   Pointers  all tensor pointers are device pointers, 16-byte aligned, owned by the caller.
  *             The library never allocates or frees device memory and keeps no device state.
  *             out must not overlap q, k, v or the workspace.
@@ -62,7 +62,8 @@ typedef struct sol_shape {
 #define SOL_QUERY_TILE 128
 
 /* Bytes of device workspace sol_attn_fwd needs for this shape and block size (0 on bad input).
- * Holds the pooled keys/values and their bf16 split copies; contents are scratch between calls. */
+ * Holds the pooled keys/values and their bf16 split copies, the pooled-key mean and covariance,
+ * the per-row thresholds and the per-row selection words; contents are scratch between calls. */
 size_t sol_attn_workspace_bytes(const sol_shape* shape, int block);
 
 /*
@@ -99,6 +100,10 @@ typedef struct sol_attn_debug {
                           round-to-nearest-even bf16 of these values) */
   int drop_unselected; /* 0: the method.  1: ablation -- unselected blocks are dropped instead of
                           pooled (a row with nothing kept then outputs 0 and lse = -inf). */
+  void* events[4];     /* hipEvent_t handles (each may be NULL), recorded on `stream` before the
+                          pooling kernel, before the pooled-key statistics, before the fused
+                          attention kernel and after it (so [2]..[3] brackets the fused kernel
+                          alone): per-kernel timing without changing the work done. */
 } sol_attn_debug;
 
 /* sol_attn_fwd plus the optional outputs above (dbg may be NULL, then identical to sol_attn_fwd). */

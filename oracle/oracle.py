@@ -55,6 +55,8 @@ def load(path: str = _LIB):
     lib.sol_oracle_dense_rows.argtypes = [p, p, p, i64, ci, p, i64, p, p]
     for f in ("sol_oracle_pool", "sol_oracle_rows", "sol_oracle_select", "sol_oracle_dense_rows"):
         getattr(lib, f).restype = ci
+    lib.sol_oracle_threads.argtypes = []
+    lib.sol_oracle_threads.restype = ci
     _lib_cache[path] = lib
     return lib
 
@@ -197,3 +199,8 @@ def tile_union_density(sel: np.ndarray, N: int, block: int, tile: int = 128) -> 
         kept += int(u.sum())
         units += int((r1 - r0) * n[u].sum())
     return kept, T * M, units
+
+
+def threads(lib=None) -> int:
+    """OpenMP threads the oracle runs on."""
+    return int((lib or load()).sol_oracle_threads())

@@ -29,6 +29,7 @@
  * results do not depend on the thread count.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -297,3 +298,6 @@ int sol_oracle_dense_rows(const float* q, const float* k, const float* v, int64_
   }
   return status;
 }
+
+/* Threads the OpenMP loops above use (for reporting the CPU baseline's core count). */
+int sol_oracle_threads(void) { return omp_get_max_threads(); }

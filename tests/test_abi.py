@@ -69,8 +69,9 @@ def test_workspace_bytes(lib):
     n = lib.sol_attn_workspace_bytes(ctypes.byref(s), 128)
     M = math.ceil(75600 / 128)
     Mp = math.ceil(M / 32) * 32
-    lower = 40 * M * 128 * 4 + 40 * 128 * 4 + 3 * 40 * Mp * 128 * 2 + 2 * 40 * 128 * Mp * 2
-    assert lower <= n <= lower + 4 * 256
+    lower = (40 * M * 128 * 4 + 40 * 128 * 4 + 40 * 128 * 8 + 3 * 40 * 128 * 128 * 2
+             + 3 * 40 * Mp * 128 * 2 + 2 * 40 * Mp * 128 * 2 + 40 * 75600 * 4 + 40 * 75600 * (Mp // 32) * 4)
+    assert lower <= n <= lower + 8 * 256
     assert lib.sol_attn_workspace_bytes(ctypes.byref(_shape(d=96)), 128) == 0
     assert lib.sol_attn_workspace_bytes(ctypes.byref(_shape()), 32) == 0
     assert lib.sol_attn_workspace_bytes(None, 128) == 0
@@ -108,7 +109,7 @@ def test_attn_fwd_rejects(lib, case):
     elif case == "zero_heads":
         s.H = 0
     elif case == "huge_n":
-        s.N = (1 << 30) + 1
+        s.N = (1 << 22) + 1
     elif case == "no_workspace":
         ws = None
         expect = solattn.SOL_EWORKSPACE
