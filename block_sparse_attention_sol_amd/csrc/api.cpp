@@ -39,7 +39,7 @@ int64_t padded_blocks(int64_t N, int block) { return (n_blocks(N, block) + 31) /
 
 // Offsets of the workspace regions (all 256-byte aligned).
 struct Workspace {
-  size_t kbar, kglob, kglob64, cp, kp, vbp, tau, rowmask, total;
+  size_t kbar, kglob, kglob64, cp, kp, vbt, tau, rowmask, total;
 };
 
 Workspace layout(const sol_shape& s, int block) {
@@ -52,8 +52,8 @@ Workspace layout(const sol_shape& s, int block) {
   w.kglob64 = w.kglob + align_up((size_t)(BH * s.d) * sizeof(float));
   w.cp = w.kglob64 + align_up((size_t)(BH * s.d) * sizeof(double));
   w.kp = w.cp + align_up((size_t)(3 * BH * s.d * s.d) * sizeof(uint16_t));
-  w.vbp = w.kp + align_up((size_t)(3 * BH * Mp * s.d) * sizeof(uint16_t));
-  w.tau = w.vbp + align_up((size_t)(2 * BH * Mp * s.d) * sizeof(uint16_t));
+  w.vbt = w.kp + align_up((size_t)(3 * BH * Mp * s.d) * sizeof(uint16_t));
+  w.tau = w.vbt + align_up((size_t)(BH * s.d * Mp) * sizeof(uint16_t));
   w.rowmask = w.tau + align_up((size_t)(BH * s.N) * sizeof(float));
   w.total = w.rowmask + align_up((size_t)(BH * s.N * (Mp / 32)) * sizeof(uint32_t));
   return w;
@@ -176,7 +176,7 @@ int sol_attn_fwd_ex(const sol_shape* shape, const void* q, const void* k, const 
   double* kglob64 = (double*)(ws + w.kglob64);
   uint16_t* cp = (uint16_t*)(ws + w.cp);
   uint16_t* kp = (uint16_t*)(ws + w.kp);
-  uint16_t* vbp = (uint16_t*)(ws + w.vbp);
+  uint16_t* vbt = (uint16_t*)(ws + w.vbt);
   float* tau = (float*)(ws + w.tau);
   uint32_t* rowmask = (dbg && dbg->mask) ? dbg->mask : (uint32_t*)(ws + w.rowmask);
   hipStream_t s = (hipStream_t)stream;
@@ -187,7 +187,7 @@ int sol_attn_fwd_ex(const sol_shape* shape, const void* q, const void* k, const 
   };
   hipError_t e = mark(0);
   if (e != hipSuccess) return hip_status(e, "event record");
-  e = solattn::launch_pool(d, BH, shape->N, block, k, v, kbar, nullptr, kp, vbp, Mp, s);
+  e = solattn::launch_pool(d, BH, shape->N, block, k, v, kbar, nullptr, kp, vbt, Mp, s);
   if (e != hipSuccess) return hip_status(e, "pool kernel launch");
   if ((e = mark(1)) != hipSuccess) return hip_status(e, "event record");
   e = solattn::launch_kstats(d, BH, M, kbar, kglob, kglob64, cp, s);
@@ -215,7 +215,7 @@ int sol_attn_fwd_ex(const sol_shape* shape, const void* q, const void* k, const 
   a.v = (const uint16_t*)v;
   a.out = (uint16_t*)out;
   a.kp = kp;
-  a.vbp = vbp;
+  a.vbt = vbt;
   a.tau = tau;
   a.rowmask = rowmask;
   a.BH = BH;

@@ -23,7 +23,7 @@
 //                    the three bf16 pieces of Kbar, the selection bits s >= tau (per row, to the
 //                    row-mask buffer) and their union over the tile (LDS), and every unselected
 //                    block's pooled token folded into the running softmax (P Vbar on the matrix
-//                    cores, Vbar as hi + lo bf16).
+//                    cores).  The chunks are double buffered like the exact stages.
 //                    Exact loop over the blocks in the union, in stages of 64 keys, double
 //                    buffered: K and V rows go straight from memory to LDS (global_load_lds), the
 //                    next stage's copy overlapping this stage's math; S^T = K Q^T, rows that did not
@@ -182,8 +182,63 @@ __device__ __forceinline__ void pv32(const lds_u8* vtile, int kr0, const uint32_
   }
 }
 
+// Vbar^T chunk tile: D rows (head dimension) x 32 blocks, 64-byte rows of four 16-byte chunks,
+// chunk index XOR (row / 4) % 4 so that 16 consecutive rows read at one position are spread over
+// the banks.  Copied with global_load_lds from vbt [D][Mp] (block index contiguous).
+template <int D>
+__device__ __forceinline__ int vbt_off(int row, int ch) { return row * 64 + ((ch ^ ((row >> 2) & 3)) << 4); }
+
+template <int D>
+__device__ __forceinline__ void load_vbt_chunk(const uint16_t* __restrict__ vt, int64_t Mp, int cb,
+                                               lds_u8* tile) {
+  constexpr int kIters = D * 4 / kThreads;
+  static_assert(D * 4 % kThreads == 0, "tile must split into whole wave loads");
+  const int t = threadIdx.x;
+  const int wave = t >> 6;
+#pragma unroll
+  for (int i = 0; i < kIters; ++i) {
+    const int p = i * kThreads + t;
+    const int row = p >> 2;
+    const int ch = (p & 3) ^ ((row >> 2) & 3);
+    const uint16_t* g = vt + (int64_t)row * Mp + (int64_t)cb * 32 + ch * 8;
+    lds_u8* dst = tile + (i * kThreads + wave * 64) * 16;
+    __builtin_amdgcn_global_load_lds((const void*)g, (__attribute__((address_space(3))) void*)dst,
+                                     16, 0, 0);
+  }
+}
+
+// O^T[ds] += Vbar^T P^T for the 32 pooled blocks of a chunk (probability registers as in pv32).
+// The A operand for blocks {16 e2 + 4 h + 0..3} and {16 e2 + 8 + 4 h + 0..3} of this lane's d row
+// is two 8-byte reads of the transposed tile.
+template <int D>
+__device__ __forceinline__ void pv_pooled(const lds_u8* vt, const uint32_t* pk, f32x16 (&o)[D / 32]) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int e2 = 0; e2 < 2; ++e2) {
+    const bf16x8 b = p_operand(pk, e2);
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds) {
+      const int row = 32 * ds + c;
+      const u32x2 x0 = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
+          vt + vbt_off<D>(row, 2 * e2) + 8 * h);
+      const u32x2 x1 = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
+          vt + vbt_off<D>(row, 2 * e2 + 1) + 8 * h);
+      u32x4 raw;
+      raw[0] = x0[0]; raw[1] = x0[1]; raw[2] = x1[0]; raw[3] = x1[1];
+      o[ds] = mfma32(__builtin_bit_cast(bf16x8, raw), b, o[ds]);
+    }
+  }
+}
+
 // Key offset (within a 32-key score block) of result register v for lane half h.
 __device__ __forceinline__ int key_of(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
+
+// The running max is only raised when a row's new scores exceed it by more than 2^kSlack
+// (log2 units); otherwise probabilities up to 2^kSlack are accumulated against the old max, which
+// fp32 sums and bf16 probabilities represent without loss.  Rescaling the accumulators is then
+// rare, and is skipped by the whole wave when no lane needs it.
+constexpr float kSlack = 8.0f;
 
 // One 64-key stage (K and V tiles in LDS) folded into this lane's running softmax.
 // active: this row takes part; nvalid: keys of the stage below N.
@@ -198,40 +253,43 @@ __device__ __forceinline__ void exact_stage(const lds_u8* ktile, const lds_u8* v
 #pragma unroll
   for (int kb = 0; kb < NS; ++kb) s[kb] = scores32<D>(ktile, 32 * kb, qf, f32x16{});
 
-  float mt = -INFINITY;
-  if (nvalid >= kStage) {
-#pragma unroll
-    for (int kb = 0; kb < NS; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[kb][v]);
-  } else {
+  const bool partial = nvalid < kStage;  // wave-uniform
+  if (partial) {
 #pragma unroll
     for (int kb = 0; kb < NS; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        if (32 * kb + key_of(v, h) < nvalid) mt = fmaxf(mt, s[kb][v]);
+        if (32 * kb + key_of(v, h) >= nvalid) s[kb][v] = -INFINITY;
   }
-  mt = fmaxf(mt, swap_halves(mt));
-  const float mnew = active ? fmaxf(mrun, mt * sl2) : mrun;
-  const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
-  mrun = mnew;
+  float mt = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < NS; ++kb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[kb][v]);
+  mt = fmaxf(mt, swap_halves(mt)) * sl2;
+  const bool grow = active && mt > mrun + kSlack;
+  if (__builtin_amdgcn_ballot_w64(grow)) {
+    const float mnew = grow ? mt : mrun;
+    const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+    mrun = mnew;
+    lsum *= alpha;
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[ds][v] *= alpha;
+  }
+  // rows that do not take part subtract +inf: every probability is 0
+  const float moff = active ? -mrun : -INFINITY;
   uint32_t pk[NS][8];
   float ps = 0.f;
 #pragma unroll
   for (int kb = 0; kb < NS; ++kb) {
     float p[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const bool ok = active && (32 * kb + key_of(v, h) < nvalid);
-      p[v] = ok ? __builtin_amdgcn_exp2f(fmaf(s[kb][v], sl2, -mnew)) : 0.f;
-    }
+    for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(fmaf(s[kb][v], sl2, moff));
     ps = round_p(p, pk[kb], ps);
   }
-  lsum = lsum * alpha + ps;
-#pragma unroll
-  for (int ds = 0; ds < D / 32; ++ds)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) o[ds][v] *= alpha;
+  lsum += ps;
 #pragma unroll
   for (int kb = 0; kb < NS; ++kb) pv32<D>(vtile, 32 * kb, pk[kb], o);
 }
@@ -381,7 +439,9 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
   constexpr int kTileBytes = kStage * D * 2;          // one 64-row tile
   constexpr int kStageBytes = 2 * kTileBytes;         // K + V
   constexpr int kChunkTile = 32 * D * 2;              // one 32-row pooled tile
-  constexpr int kRegionA = 2 * kStageBytes > 5 * kChunkTile ? 2 * kStageBytes : 5 * kChunkTile;
+  constexpr int kRouteBuf = 4 * kChunkTile;           // Kbar lo, mid, hi + Vbar^T
+  constexpr int kChunkLoads = 3 * tile_loads<D, 32>() + D * 4 / kThreads;
+  constexpr int kRegionA = 2 * kStageBytes > 2 * kRouteBuf ? 2 * kStageBytes : 2 * kRouteBuf;
   constexpr int kStagesPerBlock = BLK / kStage;
   constexpr int kLoadsPerStage = 2 * tile_loads<D, kStage>();
   uint32_t* umask = (uint32_t*)(smem_raw + kRegionA);
@@ -416,37 +476,45 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
   for (int i = t; i < W; i += kThreads) umask[i] = 0u;
 
   // ---- pooled sweep: selection bits, tile union, pooled tokens ----
+  // Chunks of 32 blocks, double buffered: chunk tiles 0..2 = lo, mid, hi pieces of Kbar,
+  // tile 3 = Vbar^T (D rows x 32 blocks).
   const int64_t piece = a.BH * a.Mp * D;
   const uint16_t* kp0 = a.kp + bh * a.Mp * D;  // hi; mid at + piece, lo at + 2 piece
-  const uint16_t* vp0 = a.vbp + bh * a.Mp * D; // hi; lo at + piece
+  const uint16_t* vt0 = a.vbt + bh * D * a.Mp;
   f32x16 o[D / 32];
 #pragma unroll
   for (int ds = 0; ds < D / 32; ++ds) o[ds] = f32x16{};
   float mrun = -1e30f;  // running max, log2 domain
   float lsum = 0.f;
-  const int64_t nchunks = a.Mp / 32;
-  for (int64_t cb = 0; cb < nchunks; ++cb) {
-    __syncthreads();
-    // pooled tiles: 0 lo, 1 mid, 2 hi pieces of Kbar; 3 Vbar hi, 4 Vbar lo
-    load_tile<D, 32>(kp0 + 2 * piece, cb * 32, a.Mp, smem + 0 * kChunkTile);
-    load_tile<D, 32>(kp0 + 1 * piece, cb * 32, a.Mp, smem + 1 * kChunkTile);
-    load_tile<D, 32>(kp0, cb * 32, a.Mp, smem + 2 * kChunkTile);
-    if (!a.drop) {
-      load_tile<D, 32>(vp0, cb * 32, a.Mp, smem + 3 * kChunkTile);
-      load_tile<D, 32>(vp0 + piece, cb * 32, a.Mp, smem + 4 * kChunkTile);
+  const int nchunks = (int)(a.Mp / 32);
+  auto issue_chunk = [&](int cb, int b) {
+    lds_u8* base = smem + b * kRouteBuf;
+    load_tile<D, 32>(kp0 + 2 * piece, (int64_t)cb * 32, a.Mp, base);
+    load_tile<D, 32>(kp0 + 1 * piece, (int64_t)cb * 32, a.Mp, base + kChunkTile);
+    load_tile<D, 32>(kp0, (int64_t)cb * 32, a.Mp, base + 2 * kChunkTile);
+    load_vbt_chunk<D>(vt0, a.Mp, cb, base + 3 * kChunkTile);
+  };
+  issue_chunk(0, 0);
+  for (int cb = 0; cb < nchunks; ++cb) {
+    const int b = cb & 1;
+    if (cb + 1 < nchunks) {
+      issue_chunk(cb + 1, b ^ 1);
+      wait_vmcnt<kChunkLoads>();
+    } else {
+      wait_vmcnt<0>();
     }
-    wait_vmcnt<0>();
-    __syncthreads();
+    bar();
+    const lds_u8* base = smem + b * kRouteBuf;
     f32x16 acc = {};
 #pragma unroll
-    for (int p = 0; p < 3; ++p) acc = scores32<D>(smem + p * kChunkTile, 0, qf, acc);
+    for (int p = 0; p < 3; ++p) acc = scores32<D>(base + p * kChunkTile, 0, qf, acc);
     uint32_t bits = 0u;
     float x[16];
     float cmax = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int kj = key_of(v, h);
-      const int64_t j = cb * 32 + kj;
+      const int64_t j = (int64_t)cb * 32 + kj;
       const bool valid = j < a.M;
       const bool sel = valid && (acc[v] * inv_sqrt_d >= tau);
       bits |= (sel ? 1u : 0u) << kj;
@@ -461,23 +529,27 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
     if (lane == 0 && u) atomicOr(&umask[cb], u);
     if (!a.drop) {
       cmax = fmaxf(cmax, swap_halves(cmax));
-      const float mnew = fmaxf(mrun, cmax);
-      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
-      mrun = mnew;
+      const bool grow = cmax > mrun + kSlack;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float mnew = grow ? cmax : mrun;
+        const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+        mrun = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int ds = 0; ds < D / 32; ++ds)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[ds][v] *= alpha;
+      }
       float p[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(x[v] - mnew);
+      for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(x[v] - mrun);
       uint32_t pk[8];
-      lsum = round_p(p, pk, lsum * alpha);
-#pragma unroll
-      for (int ds = 0; ds < D / 32; ++ds)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[ds][v] *= alpha;
-      pv32<D>(smem + 4 * kChunkTile, 0, pk, o);  // Vbar lo
-      pv32<D>(smem + 3 * kChunkTile, 0, pk, o);  // Vbar hi
+      lsum = round_p(p, pk, lsum);
+      pv_pooled<D>(base + 3 * kChunkTile, pk, o);
     }
+    bar();
   }
-  __syncthreads();
+  __syncthreads();  // union complete before the exact loop reads it
 
   // ---- exact attention over the kept blocks, double-buffered 64-key stages ----
   // Stage iterator: blocks j in the tile's union (ascending), stages s of each block with keys
@@ -619,8 +691,8 @@ __global__ __launch_bounds__(kThreads, 2) void dense_attn_kernel(const uint16_t*
 
 static size_t sparse_smem_bytes(int d, int64_t Mp) {
   const size_t stage = (size_t)2 * kStage * d * 2;
-  const size_t chunk = (size_t)5 * 32 * d * 2;
-  const size_t regionA = 2 * stage > chunk ? 2 * stage : chunk;
+  const size_t route = (size_t)4 * 32 * d * 2;
+  const size_t regionA = 2 * stage > 2 * route ? 2 * stage : 2 * route;
   return regionA + (size_t)(Mp / 32) * 4;
 }
 

@@ -6,10 +6,10 @@
 
 namespace solattn {
 
-// Pooled K/V of every key block.  kp / vbp (and Mp) only for the attention workspace; NULL in
+// Pooled K/V of every key block.  kp / vbt (and Mp) only for the attention workspace; NULL in
 // the public pooling call.
 hipError_t launch_pool(int d, int64_t BH, int64_t N, int block, const void* k, const void* v,
-                       float* kbar, float* vbar, uint16_t* kp, uint16_t* vbp, int64_t Mp,
+                       float* kbar, float* vbar, uint16_t* kp, uint16_t* vbt, int64_t Mp,
                        hipStream_t stream);
 // Mean (fp32 and fp64) and covariance (three bf16 pieces) of the pooled keys of every head.
 hipError_t launch_kstats(int d, int64_t BH, int64_t M, const float* kbar, float* kglob,
@@ -34,7 +34,7 @@ struct SparseArgs {
   const uint16_t* v;
   uint16_t* out;
   const uint16_t* kp;   // [3][BH][Mp][d] pooled keys (hi, mid, lo)
-  const uint16_t* vbp;  // [2][BH][Mp][d] pooled values (hi, lo)
+  const uint16_t* vbt;  // [BH][d][Mp] pooled values, transposed
   const float* tau;     // [BH][N]
   uint32_t* rowmask;    // [BH][N][Mp/32] selection words (written, then read back per row)
   int64_t BH, N, M, Mp;

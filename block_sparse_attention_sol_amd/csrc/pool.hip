@@ -11,8 +11,8 @@
 // means it writes the layouts the attention kernel consumes:
 //   kp   [3][BH][Mp][d] bf16: Kbar split into hi + mid + lo bf16 pieces whose sum is the fp32
 //        value, so a bf16 matrix product over the three pieces reproduces fp32 proxies;
-//   vbp  [2][BH][Mp][d] bf16: Vbar as hi + lo bf16 pieces (row-major, like the V tiles the
-//        attention kernel stages), the values of the pooled tokens;
+//   vbt  [BH][d][Mp] bf16: Vbar transposed (block index contiguous), the A operand of the
+//        pooled tokens' P Vbar product;
 // where Mp = M rounded up to a multiple of 32; padding blocks are written as zeros.
 // Two small per-head kernels follow: the mean pooled key (fp32 and fp64) and the covariance
 // matrix of the pooled keys as three bf16 pieces, from which the attention kernel gets every
@@ -26,7 +26,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void pool_kv_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t N, int block, int64_t M,
     int64_t Mp, float* __restrict__ kbar, float* __restrict__ vbar, uint16_t* __restrict__ kp,
-    uint16_t* __restrict__ vbp) {
+    uint16_t* __restrict__ vbt) {
   constexpr int kChunks = D / 8;               // 16-byte chunks per row
   constexpr int kGroups = kThreads / kChunks;  // row groups
   __shared__ float part[2][kGroups][D];
@@ -42,10 +42,7 @@ __global__ __launch_bounds__(kThreads) void pool_kv_kernel(
       if (kp) {
         for (int p = 0; p < 3; ++p) kp[((p * gridDim.y + bh) * Mp + j) * D + t] = 0;
       }
-      if (vbp) {
-        vbp[((0 * gridDim.y + bh) * Mp + j) * D + t] = 0;
-        vbp[((1 * gridDim.y + bh) * Mp + j) * D + t] = 0;
-      }
+      if (vbt) vbt[(bh * D + t) * Mp + j] = 0;
     }
     return;
   }
@@ -97,12 +94,7 @@ __global__ __launch_bounds__(kThreads) void pool_kv_kernel(
       }
     } else {
       if (vbar) vbar[(bh * M + j) * D + c] = mean;
-      if (vbp) {
-        const uint16_t h16 = f32_to_bf16_rne(mean);
-        const uint16_t l16 = f32_to_bf16_rne(mean - bits_f32((uint32_t)h16 << 16));
-        vbp[((0 * gridDim.y + bh) * Mp + j) * D + c] = h16;
-        vbp[((1 * gridDim.y + bh) * Mp + j) * D + c] = l16;
-      }
+      if (vbt) vbt[(bh * D + c) * Mp + j] = f32_to_bf16_rne(mean);
     }
   }
 }
@@ -178,17 +170,17 @@ __global__ __launch_bounds__(kThreads) void kcov_kernel(const float* __restrict_
 }
 
 hipError_t launch_pool(int d, int64_t BH, int64_t N, int block, const void* k, const void* v,
-                       float* kbar, float* vbar, uint16_t* kp, uint16_t* vbp, int64_t Mp,
+                       float* kbar, float* vbar, uint16_t* kp, uint16_t* vbt, int64_t Mp,
                        hipStream_t stream) {
   const int64_t M = (N + block - 1) / block;
-  const int64_t gx = (kp || vbp) ? Mp : M;
+  const int64_t gx = (kp || vbt) ? Mp : M;
   dim3 grid((unsigned)gx, (unsigned)BH);
   if (d == 64)
     hipLaunchKernelGGL(pool_kv_kernel<64>, grid, dim3(kThreads), 0, stream,
-                       (const uint16_t*)k, (const uint16_t*)v, N, block, M, Mp, kbar, vbar, kp, vbp);
+                       (const uint16_t*)k, (const uint16_t*)v, N, block, M, Mp, kbar, vbar, kp, vbt);
   else
     hipLaunchKernelGGL(pool_kv_kernel<128>, grid, dim3(kThreads), 0, stream,
-                       (const uint16_t*)k, (const uint16_t*)v, N, block, M, Mp, kbar, vbar, kp, vbp);
+                       (const uint16_t*)k, (const uint16_t*)v, N, block, M, Mp, kbar, vbar, kp, vbt);
   return hipGetLastError();
 }
 

@@ -70,7 +70,7 @@ def test_workspace_bytes(lib):
     M = math.ceil(75600 / 128)
     Mp = math.ceil(M / 32) * 32
     lower = (40 * M * 128 * 4 + 40 * 128 * 4 + 40 * 128 * 8 + 3 * 40 * 128 * 128 * 2
-             + 3 * 40 * Mp * 128 * 2 + 2 * 40 * Mp * 128 * 2 + 40 * 75600 * 4 + 40 * 75600 * (Mp // 32) * 4)
+             + 3 * 40 * Mp * 128 * 2 + 40 * Mp * 128 * 2 + 40 * 75600 * 4 + 40 * 75600 * (Mp // 32) * 4)
     assert lower <= n <= lower + 8 * 256
     assert lib.sol_attn_workspace_bytes(ctypes.byref(_shape(d=96)), 128) == 0
     assert lib.sol_attn_workspace_bytes(ctypes.byref(_shape()), 32) == 0
