@@ -47,13 +47,15 @@ constexpr int kStage = 64;  // keys per pipeline stage
 
 // ---------------------------------------------------------------------------------------------
 // LDS tiles: row-major [rows][D] bf16, 16-byte chunks XOR-swizzled per row.  The swizzle makes
-// both access patterns conflict-free: 16 consecutive rows read at one logical chunk (the K / Kbar
-// A operand), and 4 consecutive rows read at two adjacent chunks (the transpose read of V).
+// both access patterns conflict-free on a 256-byte-wide LDS: 16 consecutive rows read at one
+// logical chunk (the K / Kbar A operand) land on 16 distinct 16-byte bank groups, and the
+// transpose read of V -- 4 consecutive rows x 4 adjacent chunks per 32 lanes -- lands each row
+// in its own 64-byte quarter.
 // ---------------------------------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ int swz(int row, int ch) {
-  if constexpr (D == 128) return ch ^ (((row & 7) << 1) | ((row >> 3) & 1));
-  else return ch ^ ((((row >> 1) & 3) << 1) | ((row >> 3) & 1));
+  if constexpr (D == 128) return ch ^ (((row & 3) << 2) | ((row >> 2) & 3));
+  else return ch ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int ch) {  // byte offset of a 16-byte chunk
@@ -86,6 +88,65 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ src, int6
 }
 template <int D, int ROWS>
 constexpr int tile_loads() { return ROWS * (D / 8) / kThreads; }
+
+// Buffer resource descriptor over `bytes` bytes at `base` (raw buffer: stride 0, 32-bit dword
+// data format): loads past `bytes` return zeros.  Built from wave-uniform values, so it lives in
+// scalar registers.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t addr = (uint64_t)(uintptr_t)base;
+  i32x4_t r;
+  r[0] = (int)__builtin_amdgcn_readfirstlane((uint32_t)addr);
+  r[1] = (int)__builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32) & 0xffffu);
+  r[2] = (int)__builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Per-lane byte offsets, within a ROWS-row tile of a row-major [*, D] bf16 matrix, of the 16 bytes
+// each lane copies so that the LDS tile comes out swizzled (see load_tile).
+template <int D, int ROWS>
+struct TileOffsets {
+  uint32_t v[tile_loads<D, ROWS>()];
+  __device__ __forceinline__ TileOffsets() {
+    constexpr int kChunks = D / 8;
+#pragma unroll
+    for (int i = 0; i < tile_loads<D, ROWS>(); ++i) {
+      const int p = i * kThreads + (int)threadIdx.x;
+      const int row = p / kChunks;
+      v[i] = (uint32_t)(row * D * 2 + swz<D>(row, p % kChunks) * 16);
+    }
+  }
+};
+
+// Copy the first ROWS rows of the buffer `rsrc` into LDS with buffer loads (16 bytes per lane,
+// straight to LDS).  Rows past the buffer end read as zeros: the range check covers the per-lane
+// offset, so callers start the resource at the tile (soff stays 0; a scalar offset would bypass
+// the check).
+//
+// The copy is issued as an asm statement rather than through the compiler's LDS-DMA builtin: the
+// compiler cannot tell which LDS buffer such a copy writes, and would make every LDS transpose
+// read wait for all copies in flight -- including the next stage's prefetch, serialising copy and
+// math.  The instruction has no register result (its destination is LDS), its address operands
+// are consumed at issue, and the callers order the LDS traffic themselves: wait_vmcnt before the
+// barrier that publishes a tile, and a barrier before a buffer is refilled.
+template <int D, int ROWS>
+__device__ __forceinline__ void load_tile_buf(i32x4_t rsrc, uint32_t soff,
+                                              const TileOffsets<D, ROWS>& off, lds_u8* tile) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int i = 0; i < tile_loads<D, ROWS>(); ++i) {
+    // wave-uniform destination (lane l lands at +16 l); the LDS pointer itself is an operand, so
+    // the compiler knows this statement writes there
+    lds_u8* dst = tile + (i * kThreads + wave * 64) * 16;
+    __asm__ __volatile__(
+        "s_mov_b32 m0, %[m0]\n\t"
+        "buffer_load_dwordx4 %[voff], %[rsrc], %[soff] offen lds"
+        :
+        : [m0] "s"(dst), [voff] "v"(off.v[i]), [rsrc] "s"(rsrc), [soff] "s"(soff)
+        : "memory", "m0");
+  }
+}
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 template <int N>
@@ -234,11 +295,12 @@ __device__ __forceinline__ void pv_pooled(const lds_u8* vt, const uint32_t* pk, 
 // Key offset (within a 32-key score block) of result register v for lane half h.
 __device__ __forceinline__ int key_of(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
 
-// The running max is only raised when a row's new scores exceed it by more than 2^kSlack
-// (log2 units); otherwise probabilities up to 2^kSlack are accumulated against the old max, which
-// fp32 sums and bf16 probabilities represent without loss.  Rescaling the accumulators is then
-// rare, and is skipped by the whole wave when no lane needs it.
-constexpr float kSlack = 8.0f;
+// The running max is only raised when a row's new scores exceed it by more than kSlack (log2
+// units); otherwise probabilities up to 2^kSlack are accumulated against the old max.  With
+// N <= 2^22 keys, sums stay below 2^54 times the largest |v|, far inside fp32 range, and bf16
+// probabilities keep their relative precision.  Rescaling the accumulators is then rare, and is
+// skipped by the whole wave when no lane needs it.
+constexpr float kSlack = 32.0f;
 
 // One 64-key stage (K and V tiles in LDS) folded into this lane's running softmax.
 // active: this row takes part; nvalid: keys of the stage below N.
@@ -266,7 +328,7 @@ __device__ __forceinline__ void exact_stage(const lds_u8* ktile, const lds_u8* v
   for (int kb = 0; kb < NS; ++kb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[kb][v]);
-  mt = fmaxf(mt, swap_halves(mt)) * sl2;
+  mt = pair_max(mt) * sl2;
   const bool grow = active && mt > mrun + kSlack;
   if (__builtin_amdgcn_ballot_w64(grow)) {
     const float mnew = grow ? mt : mrun;
@@ -317,7 +379,7 @@ __device__ __forceinline__ void epilogue(const f32x16 (&o)[D / 32], float mrun, 
   const int lane = threadIdx.x & 63;
   const int c = lane & 31, h = lane >> 5;
   const int64_t row = row0 + c;
-  const float l = lsum + swap_halves(lsum);
+  const float l = pair_sum(lsum);
   const float inv = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
   for (int ds = 0; ds < D / 32; ++ds)
@@ -415,8 +477,8 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(RowStatsArgs a) {
         vpart = fmaf(y[4 * g + 3], bf16_hi(qq[1]), vpart);
       }
     }
-    const float mu = (mpart + swap_halves(mpart)) * inv_sqrt_d;
-    const float var = (vpart + swap_halves(vpart)) / (float)D;
+    const float mu = pair_sum(mpart) * inv_sqrt_d;
+    const float var = pair_sum(vpart) / (float)D;
     const float sigma = sqrtf(fmaxf(var, 0.f));
     const float tau = isinf(a.beta) ? a.beta : fmaf(a.beta, sigma, mu);
     if (valid && h == 0) {
@@ -440,10 +502,8 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
   constexpr int kStageBytes = 2 * kTileBytes;         // K + V
   constexpr int kChunkTile = 32 * D * 2;              // one 32-row pooled tile
   constexpr int kRouteBuf = 4 * kChunkTile;           // Kbar lo, mid, hi + Vbar^T
-  constexpr int kChunkLoads = 3 * tile_loads<D, 32>() + D * 4 / kThreads;
   constexpr int kRegionA = 2 * kStageBytes > 2 * kRouteBuf ? 2 * kStageBytes : 2 * kRouteBuf;
   constexpr int kStagesPerBlock = BLK / kStage;
-  constexpr int kLoadsPerStage = 2 * tile_loads<D, kStage>();
   uint32_t* umask = (uint32_t*)(smem_raw + kRegionA);
   const int W = (int)(a.Mp / 32);
 
@@ -497,13 +557,9 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
   issue_chunk(0, 0);
   for (int cb = 0; cb < nchunks; ++cb) {
     const int b = cb & 1;
-    if (cb + 1 < nchunks) {
-      issue_chunk(cb + 1, b ^ 1);
-      wait_vmcnt<kChunkLoads>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    bar();
+    wait_vmcnt<0>();
+    bar();  // publishes chunk cb, retires chunk cb - 1's buffer
+    if (cb + 1 < nchunks) issue_chunk(cb + 1, b ^ 1);
     const lds_u8* base = smem + b * kRouteBuf;
     f32x16 acc = {};
 #pragma unroll
@@ -521,14 +577,14 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
       x[v] = (valid && !sel) ? fmaf(acc[v], sl2, j == a.M - 1 ? l2n_last : l2n_full) : -INFINITY;
       cmax = fmaxf(cmax, x[v]);
     }
-    const uint32_t word = bits | swap_halves_u(bits);
+    const uint32_t word = pair_or(bits);
     if (h == 0 && rvalid) rmask[row * W + cb] = word;
     uint32_t u = word;
 #pragma unroll
     for (int off = 16; off >= 1; off >>= 1) u |= (uint32_t)__shfl_xor((int)u, off, kWave);
     if (lane == 0 && u) atomicOr(&umask[cb], u);
     if (!a.drop) {
-      cmax = fmaxf(cmax, swap_halves(cmax));
+      cmax = pair_max(cmax);
       const bool grow = cmax > mrun + kSlack;
       if (__builtin_amdgcn_ballot_w64(grow)) {
         const float mnew = grow ? cmax : mrun;
@@ -547,9 +603,8 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
       lsum = round_p(p, pk, lsum);
       pv_pooled<D>(base + 3 * kChunkTile, pk, o);
     }
-    bar();
   }
-  __syncthreads();  // union complete before the exact loop reads it
+  __syncthreads();  // union complete and chunk buffers retired before the exact loop
 
   // ---- exact attention over the kept blocks, double-buffered 64-key stages ----
   // Stage iterator: blocks j in the tile's union (ascending), stages s of each block with keys
@@ -559,8 +614,7 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
   int it_j = -1, it_s = kStagesPerBlock;
   auto next_stage = [&](int& j, int& s) -> bool {
     for (;;) {
-      if (it_j >= 0 && it_s + 1 < kStagesPerBlock &&
-          (int64_t)it_j * BLK + (int64_t)(it_s + 1) * kStage < a.N) {
+      if (it_j >= 0 && it_s + 1 < kStagesPerBlock && it_j * BLK + (it_s + 1) * kStage < (int)a.N) {
         ++it_s;
         j = it_j;
         s = it_s;
@@ -576,13 +630,17 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
       it_s = -1;
     }
   };
+  const TileOffsets<D, kStage> toff;
   auto issue = [&](int j, int s, int buf) {
-    const int64_t r0 = (int64_t)j * BLK + (int64_t)s * kStage;
+    const int r0 = j * BLK + s * kStage;
+    const uint32_t bytes = (uint32_t)((int)a.N - r0) * (uint32_t)(D * 2);
     lds_u8* base = smem + buf * kStageBytes;
-    load_tile<D, kStage>(kb, r0, a.N, base);
-    load_tile<D, kStage>(vb, r0, a.N, base + kTileBytes);
+    load_tile_buf<D, kStage>(make_rsrc(kb + (int64_t)r0 * D, bytes), 0u, toff, base);
+    load_tile_buf<D, kStage>(make_rsrc(vb + (int64_t)r0 * D, bytes), 0u, toff, base + kTileBytes);
   };
 
+  // One barrier per stage: it publishes the stage's copy (each lane waited for its own loads)
+  // and retires the previous stage's reads, so the next copy can go into that buffer.
   int kept_blocks = 0;
   int cur_j = -1, cur_s = 0;
   bool have = next_stage(cur_j, cur_s);
@@ -591,32 +649,28 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
   int mask_w = -1;
   uint32_t mask_word = 0u;
   while (have) {
+    wait_vmcnt<0>();
+    bar();
     int nj = -1, ns = 0;
     const bool more = next_stage(nj, ns);
-    if (more) {
-      issue(nj, ns, buf ^ 1);
-      wait_vmcnt<kLoadsPerStage>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    bar();
+    if (more) issue(nj, ns, buf ^ 1);
     if (cur_s == 0) ++kept_blocks;
     if ((cur_j >> 5) != mask_w) {
       mask_w = cur_j >> 5;
       mask_word = rvalid ? rmask[row * W + mask_w] : 0u;
     }
     const bool active = (mask_word >> (cur_j & 31)) & 1u;
-    const int64_t r0 = (int64_t)cur_j * BLK + (int64_t)cur_s * kStage;
-    const int nvalid = (int)((a.N - r0) < kStage ? (a.N - r0) : kStage);
+    const int r0 = cur_j * BLK + cur_s * kStage;
+    const int nvalid = (int)a.N - r0 < kStage ? (int)a.N - r0 : kStage;
     const lds_u8* base = smem + buf * kStageBytes;
     exact_stage<D>(base, base + kTileBytes, qf, active, nvalid, sl2, mrun, lsum, o);
-    bar();
     buf ^= 1;
     cur_j = nj;
     cur_s = ns;
     have = more;
   }
   if (a.tile_kept && t == 0) a.tile_kept[bh * ntiles + tile] = kept_blocks;
+  bar();  // every wave is done with the stage buffers before the epilogue reuses them
 
   epilogue<D>(o, mrun, lsum, row0, a.N, a.out + bh * a.N * D,
               a.out_f32 ? a.out_f32 + bh * a.N * D : nullptr, a.lse ? a.lse + bh * a.N : nullptr,
@@ -638,7 +692,6 @@ __global__ __launch_bounds__(kThreads, 2) void dense_attn_kernel(const uint16_t*
   lds_u8* smem = (lds_u8*)smem_raw;
   constexpr int kTileBytes = kStage * D * 2;
   constexpr int kStageBytes = 2 * kTileBytes;
-  constexpr int kLoadsPerStage = 2 * tile_loads<D, kStage>();
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, c = lane & 31;
   const int64_t ntiles = (N + kQTile - 1) / kQTile;
@@ -660,27 +713,27 @@ __global__ __launch_bounds__(kThreads, 2) void dense_attn_kernel(const uint16_t*
   for (int ds = 0; ds < D / 32; ++ds) o[ds] = f32x16{};
   float mrun = -1e30f, lsum = 0.f;
 
-  const int64_t nst = (N + kStage - 1) / kStage;
-  load_tile<D, kStage>(kb, 0, N, smem);
-  load_tile<D, kStage>(vb, 0, N, smem + kTileBytes);
+  const int nst = (int)((N + kStage - 1) / kStage);
+  const TileOffsets<D, kStage> toff;
+  auto issue = [&](int st, lds_u8* base) {
+    const int r0 = st * kStage;
+    const uint32_t bytes = (uint32_t)((int)N - r0) * (uint32_t)(D * 2);
+    load_tile_buf<D, kStage>(make_rsrc(kb + (int64_t)r0 * D, bytes), 0u, toff, base);
+    load_tile_buf<D, kStage>(make_rsrc(vb + (int64_t)r0 * D, bytes), 0u, toff, base + kTileBytes);
+  };
+  issue(0, smem);
   int buf = 0;
-  for (int64_t st = 0; st < nst; ++st) {
-    if (st + 1 < nst) {
-      lds_u8* nbase = smem + (buf ^ 1) * kStageBytes;
-      load_tile<D, kStage>(kb, (st + 1) * kStage, N, nbase);
-      load_tile<D, kStage>(vb, (st + 1) * kStage, N, nbase + kTileBytes);
-      wait_vmcnt<kLoadsPerStage>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    bar();
-    const int64_t r0 = st * kStage;
-    const int nvalid = (int)((N - r0) < kStage ? (N - r0) : kStage);
+  for (int st = 0; st < nst; ++st) {
+    wait_vmcnt<0>();
+    bar();  // publishes stage st, retires stage st - 1's buffer
+    if (st + 1 < nst) issue(st + 1, smem + (buf ^ 1) * kStageBytes);
+    const int r0 = st * kStage;
+    const int nvalid = (int)N - r0 < kStage ? (int)N - r0 : kStage;
     const lds_u8* base = smem + buf * kStageBytes;
     exact_stage<D>(base, base + kTileBytes, qf, true, nvalid, sl2, mrun, lsum, o);
-    bar();
     buf ^= 1;
   }
+  bar();  // stage buffers free for the epilogue
   epilogue<D>(o, mrun, lsum, row0, N, out + bh * N * D, nullptr, lse ? lse + bh * N : nullptr,
               smem + wave * 32 * D * 2);
 }

@@ -58,12 +58,29 @@ __device__ __forceinline__ float add_bf16x2(uint32_t packed, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
 }
 
-// Exchange a value with the lane in the other half of the wave (l <-> l ^ 32).
-__device__ __forceinline__ float swap_halves(float x) {
-  return __shfl_xor(x, 32, kWave);
+// Lane-pair combines across the two halves of the wave (lane l with lane l ^ 32), with the
+// gfx950 v_permlane32_swap (a VALU op, no LDS round trip).  Swapping a register with itself
+// leaves lanes 0-31 of the first result and lanes 32-63 of the second holding x, the other
+// halves holding the partner's x, so any symmetric combine of the two results is the pair value.
+__device__ __forceinline__ void pair_values(uint32_t x, uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  a = r[0];
+  b = r[1];
 }
-__device__ __forceinline__ uint32_t swap_halves_u(uint32_t x) {
-  return (uint32_t)__shfl_xor((int)x, 32, kWave);
+__device__ __forceinline__ float pair_max(float x) {
+  uint32_t a, b;
+  pair_values(__builtin_bit_cast(uint32_t, x), a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  uint32_t a, b;
+  pair_values(__builtin_bit_cast(uint32_t, x), a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ uint32_t pair_or(uint32_t x) {
+  uint32_t a, b;
+  pair_values(x, a, b);
+  return a | b;
 }
 
 // LDS row-major tile with rows of `kChunks` 16-byte chunks; chunk index XOR-swizzled by the row so
