@@ -44,6 +44,7 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kStage = 64;  // keys per pipeline stage
+constexpr int kRowStatsTiles = 16;  // query tiles per row-statistics workgroup (C staged once)
 
 // ---------------------------------------------------------------------------------------------
 // LDS tiles: row-major [rows][D] bf16, 16-byte chunks XOR-swizzled per row.  The swizzle makes
@@ -139,12 +140,16 @@ __device__ __forceinline__ void load_tile_buf(i32x4_t rsrc, uint32_t soff,
     // wave-uniform destination (lane l lands at +16 l); the LDS pointer itself is an operand, so
     // the compiler knows this statement writes there
     lds_u8* dst = tile + (i * kThreads + wave * 64) * 16;
+    // m0 (the LDS destination base of the copy) is saved and restored around the copy
+    uint32_t saved;
     __asm__ __volatile__(
+        "s_mov_b32 %[saved], m0\n\t"
         "s_mov_b32 m0, %[m0]\n\t"
-        "buffer_load_dwordx4 %[voff], %[rsrc], %[soff] offen lds"
-        :
+        "buffer_load_dwordx4 %[voff], %[rsrc], %[soff] offen lds\n\t"
+        "s_mov_b32 m0, %[saved]"
+        : [saved] "=&s"(saved)
         : [m0] "s"(dst), [voff] "v"(off.v[i]), [rsrc] "s"(rsrc), [soff] "s"(soff)
-        : "memory", "m0");
+        : "memory");
   }
 }
 
@@ -429,9 +434,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void rowstats_kernel(RowStatsArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   lds_u8* smem = (lds_u8*)smem_raw;
-  constexpr int kTilesPerWg = 4;
   const int64_t ntiles = (a.N + kQTile - 1) / kQTile;
-  const int64_t groups = (ntiles + kTilesPerWg - 1) / kTilesPerWg;
+  const int64_t groups = (ntiles + kRowStatsTiles - 1) / kRowStatsTiles;
   const int64_t bh = blockIdx.x / groups;
   const int64_t grp = blockIdx.x % groups;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane & 31, h = lane >> 5;
@@ -447,36 +451,53 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(RowStatsArgs a) {
 
   const float inv_sqrt_d = 1.0f / sqrtf((float)D);
   const float* kg = a.kglob + bh * D;
-  for (int tt = 0; tt < kTilesPerWg; ++tt) {
-    const int64_t tile = grp * kTilesPerWg + tt;
+  for (int tt = 0; tt < kRowStatsTiles; ++tt) {
+    const int64_t tile = grp * kRowStatsTiles + tt;
     if (tile >= ntiles) break;
     const int64_t row = tile * kQTile + wave * 32 + c;
     const bool valid = row < a.N;
     const uint16_t* qrow = a.q + (bh * a.N + row) * D;
     bf16x8 qf[D / 16];
     load_q<D>(qrow, valid, qf);
+    // query values in the layout of C q's rows (a = 32 ab + 8 g + 4 h + 0..3)
+    u32x2 qa[D / 32][4];
+#pragma unroll
+    for (int ab = 0; ab < D / 32; ++ab)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 qq = {0u, 0u};
+        if (valid) qq = *reinterpret_cast<const u32x2*>(qrow + 32 * ab + 8 * g + 4 * h);
+        qa[ab][g] = qq;
+      }
     float mpart = 0.f;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) mpart = fmaf((float)qf[kk][e], kg[16 * kk + 8 * h + e], mpart);
+    // y[ab][v] = (C q)[32 ab + 8 (v/4) + 4 h + v%4]: D/32 independent accumulation chains,
+    // pieces smallest first
+    f32x16 y[D / 32];
+#pragma unroll
+    for (int ab = 0; ab < D / 32; ++ab) y[ab] = f32x16{};
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+        for (int ab = 0; ab < D / 32; ++ab) {
+          const u32x4 raw = lds_read16(smem + p * D * D * 2 + tile_off<D>(32 * ab + c, 2 * kk + h));
+          y[ab] = mfma32(__builtin_bit_cast(bf16x8, raw), qf[kk], y[ab]);
+        }
     float vpart = 0.f;
 #pragma unroll
-    for (int ab = 0; ab < D / 32; ++ab) {
-      f32x16 y = {};
-#pragma unroll
-      for (int p = 0; p < 3; ++p) y = scores32<D>(smem + p * D * D * 2, 32 * ab, qf, y);
-      // y[v] = (C q)[a], a = 32 ab + 8 (v/4) + 4 h + v%4
+    for (int ab = 0; ab < D / 32; ++ab)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        u32x2 qq = {0u, 0u};
-        if (valid) qq = *reinterpret_cast<const u32x2*>(qrow + 32 * ab + 8 * g + 4 * h);
-        vpart = fmaf(y[4 * g + 0], bf16_lo(qq[0]), vpart);
-        vpart = fmaf(y[4 * g + 1], bf16_hi(qq[0]), vpart);
-        vpart = fmaf(y[4 * g + 2], bf16_lo(qq[1]), vpart);
-        vpart = fmaf(y[4 * g + 3], bf16_hi(qq[1]), vpart);
+        vpart = fmaf(y[ab][4 * g + 0], bf16_lo(qa[ab][g][0]), vpart);
+        vpart = fmaf(y[ab][4 * g + 1], bf16_hi(qa[ab][g][0]), vpart);
+        vpart = fmaf(y[ab][4 * g + 2], bf16_lo(qa[ab][g][1]), vpart);
+        vpart = fmaf(y[ab][4 * g + 3], bf16_hi(qa[ab][g][1]), vpart);
       }
-    }
     const float mu = pair_sum(mpart) * inv_sqrt_d;
     const float var = pair_sum(vpart) / (float)D;
     const float sigma = sqrtf(fmaxf(var, 0.f));
@@ -526,6 +547,8 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
   bf16x8 qf[D / 16];
   load_q<D>(qb + row * D, rvalid, qf);
   const float tau = rvalid ? a.tau[bh * a.N + row] : INFINITY;  // padding rows keep nothing
+  // s >= tau  <=>  raw dot product >= tau * sqrt(d)  (compared in fp32)
+  const float tau_raw = tau * sqrtf((float)D);
 
   const float inv_sqrt_d = 1.0f / sqrtf((float)D);
   const float sl2 = inv_sqrt_d * kLog2e;
@@ -567,22 +590,32 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
     uint32_t bits = 0u;
     float x[16];
     float cmax = -INFINITY;
+    const int nvalid = (int)(a.M - (int64_t)cb * 32);  // blocks of this chunk below M
+    if (nvalid >= 32) {  // wave-uniform: every block of the chunk exists and is full-size
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int kj = key_of(v, h);
-      const int64_t j = (int64_t)cb * 32 + kj;
-      const bool valid = j < a.M;
-      const bool sel = valid && (acc[v] * inv_sqrt_d >= tau);
-      bits |= (sel ? 1u : 0u) << kj;
-      x[v] = (valid && !sel) ? fmaf(acc[v], sl2, j == a.M - 1 ? l2n_last : l2n_full) : -INFINITY;
-      cmax = fmaxf(cmax, x[v]);
+      for (int v = 0; v < 16; ++v) {
+        const int kj = key_of(v, h);
+        const bool sel = acc[v] >= tau_raw;
+        bits |= (sel ? 1u : 0u) << kj;
+        x[v] = sel ? -INFINITY : fmaf(acc[v], sl2, l2n_full);
+        cmax = fmaxf(cmax, x[v]);
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kj = key_of(v, h);
+        const bool valid = kj < nvalid;
+        const bool sel = valid && acc[v] >= tau_raw;
+        bits |= (sel ? 1u : 0u) << kj;
+        x[v] = (valid && !sel) ? fmaf(acc[v], sl2, kj == nvalid - 1 ? l2n_last : l2n_full)
+                               : -INFINITY;
+        cmax = fmaxf(cmax, x[v]);
+      }
     }
     const uint32_t word = pair_or(bits);
     if (h == 0 && rvalid) rmask[row * W + cb] = word;
-    uint32_t u = word;
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) u |= (uint32_t)__shfl_xor((int)u, off, kWave);
-    if (lane == 0 && u) atomicOr(&umask[cb], u);
+    // tile union: one LDS atomic OR per row (no dependent cross-lane reduction)
+    if (h == 0 && word) atomicOr(&umask[cb], word);
     if (!a.drop) {
       cmax = pair_max(cmax);
       const bool grow = cmax > mrun + kSlack;
@@ -782,7 +815,7 @@ static hipError_t launch_rowstats_t(const RowStatsArgs& a, hipStream_t stream) {
   hipError_t err = set_smem(kern, smem);
   if (err != hipSuccess) return err;
   const int64_t ntiles = (a.N + kQTile - 1) / kQTile;
-  const int64_t groups = (ntiles + 3) / 4;
+  const int64_t groups = (ntiles + kRowStatsTiles - 1) / kRowStatsTiles;
   hipLaunchKernelGGL(kern, dim3((unsigned)(a.BH * groups)), dim3(kThreads), smem, stream, a);
   return hipGetLastError();
 }

@@ -14,9 +14,9 @@
 //   vbt  [BH][d][Mp] bf16: Vbar transposed (block index contiguous), the A operand of the
 //        pooled tokens' P Vbar product;
 // where Mp = M rounded up to a multiple of 32; padding blocks are written as zeros.
-// Two small per-head kernels follow: the mean pooled key (fp32 and fp64) and the covariance
-// matrix of the pooled keys as three bf16 pieces, from which the attention kernel gets every
-// query's proxy standard deviation as a quadratic form.
+// A small per-head kernel follows: the mean pooled key (fp32 and fp64) and the covariance matrix
+// of the pooled keys as three bf16 pieces, from which every query's proxy standard deviation is a
+// quadratic form.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -99,74 +99,84 @@ __global__ __launch_bounds__(kThreads) void pool_kv_kernel(
   }
 }
 
-// Mean of the pooled keys of each head, accumulated in fp64: kglob[bh][c] = (1/M) sum_j Kbar_j[c].
-// The mean proxy score of a query is then q . kglob / sqrt(d) (the mean is linear).
+// Mean and covariance of the pooled keys of each head, in fp64:
+//   g[a] = (1/M) sum_j Kbar_j[a],   C[a][b] = (1/M) sum_j Kbar_j[a] Kbar_j[b] - g[a] g[b].
+// The mean proxy score of a query is q . g / sqrt(d) (the mean is linear), and for the proxy row
+// s_ij = q_i . Kbar_j / sqrt(d) the population variance over j is exactly q_i^T C q_i / d.  C is
+// rounded to fp32 and written as hi + mid + lo bf16 pieces cp [3][BH][D][D] (their sum is the fp32
+// value), so a bf16 matrix product with fp32 accumulation evaluates C q to fp32 accuracy.
+// One workgroup computes a 32 x 32 tile of C: pooled keys are staged through LDS in chunks of 64
+// blocks, each thread accumulates a 2 x 2 block of products and the two column sums.  The diagonal
+// tiles (ai == bi) also write g (fp32 and fp64).
 template <int D>
-__global__ __launch_bounds__(kThreads) void kglob_kernel(const float* __restrict__ kbar, int64_t M,
-                                                         float* __restrict__ kglob,
-                                                         double* __restrict__ kglob64) {
-  constexpr int kGroups = kThreads / D;
-  __shared__ double part[kGroups][D];
-  const int64_t bh = blockIdx.x;
+__global__ __launch_bounds__(kThreads) void kstats_kernel(const float* __restrict__ kbar, int64_t M,
+                                                          float* __restrict__ kglob,
+                                                          double* __restrict__ kglob64,
+                                                          uint16_t* __restrict__ cp) {
+  constexpr int kT = D / 32;  // tiles per dimension
+  constexpr int kChunk = 64;
+  __shared__ double sa[kChunk][32];
+  __shared__ double sb[kChunk][32];
+  const int64_t bh = blockIdx.x / (kT * kT);
+  const int ai = (int)(blockIdx.x % (kT * kT)) / kT;
+  const int bi = (int)(blockIdx.x % (kT * kT)) % kT;
   const int t = threadIdx.x;
-  const int c = t % D;
-  const int g = t / D;
-  double s = 0.0;
-  for (int64_t j = g; j < M; j += kGroups) s += (double)kbar[(bh * M + j) * D + c];
-  part[g][c] = s;
-  __syncthreads();
-  if (t < D) {
-    double tot = 0.0;
-    for (int q = 0; q < kGroups; ++q) tot += part[q][t];
-    kglob[bh * D + t] = (float)(tot / (double)M);
-    kglob64[bh * D + t] = tot / (double)M;
-  }
-}
-
-// Covariance of the pooled keys of each head, in fp64:
-//   C[a][b] = (1/M) sum_j (Kbar_j[a] - g[a]) (Kbar_j[b] - g[b]),  g = mean_j Kbar_j.
-// For the proxy row s_ij = q_i . Kbar_j / sqrt(d), the population variance over j is exactly
-// q_i^T C q_i / d.  C is rounded to fp32 and written as hi + mid + lo bf16 pieces
-// cp [3][BH][D][D] (their sum is the fp32 value), so a bf16 matrix product with fp32
-// accumulation evaluates C q to fp32 accuracy.  One workgroup computes 8 rows of C.
-template <int D>
-__global__ __launch_bounds__(kThreads) void kcov_kernel(const float* __restrict__ kbar, int64_t M,
-                                                        const double* __restrict__ kglob64,
-                                                        uint16_t* __restrict__ cp) {
-  constexpr int kRows = 8;
-  constexpr int kPer = kRows * D / kThreads;  // entries per thread
-  const int64_t bh = blockIdx.x;
-  const int a0 = blockIdx.y * kRows;
-  const int t = threadIdx.x;
+  const int ta = t / 16, tb = t % 16;  // rows 2 ta + {0,1}, columns 2 tb + {0,1} of the tile
   const float* kb = kbar + bh * M * D;
-  const double* g = kglob64 + bh * D;
-  double acc[kPer];
-  int ra[kPer], cb[kPer];
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int idx = e * kThreads + t;
-    ra[e] = a0 + idx / D;
-    cb[e] = idx % D;
-    acc[e] = 0.0;
+  double c00 = 0.0, c01 = 0.0, c10 = 0.0, c11 = 0.0;
+  double s1a = 0.0, s1b = 0.0;  // column sums (threads t < 32: a column t, b column t)
+  for (int64_t j0 = 0; j0 < M; j0 += kChunk) {
+    const int n = (int)((M - j0) < kChunk ? (M - j0) : kChunk);
+    __syncthreads();
+    for (int idx = t; idx < kChunk * 32; idx += kThreads) {
+      const int r = idx / 32, col = idx % 32;
+      sa[r][col] = r < n ? (double)kb[(j0 + r) * D + 32 * ai + col] : 0.0;
+      sb[r][col] = r < n ? (double)kb[(j0 + r) * D + 32 * bi + col] : 0.0;
+    }
+    __syncthreads();
+    for (int r = 0; r < n; ++r) {
+      const double a0 = sa[r][2 * ta], a1 = sa[r][2 * ta + 1];
+      const double b0 = sb[r][2 * tb], b1 = sb[r][2 * tb + 1];
+      c00 = fma(a0, b0, c00);
+      c01 = fma(a0, b1, c01);
+      c10 = fma(a1, b0, c10);
+      c11 = fma(a1, b1, c11);
+    }
+    if (t < 32) {
+      for (int r = 0; r < n; ++r) {
+        s1a += sa[r][t];
+        s1b += sb[r][t];
+      }
+    }
   }
-  for (int64_t j = 0; j < M; ++j) {
-#pragma unroll
-    for (int e = 0; e < kPer; ++e)
-      acc[e] += ((double)kb[j * D + ra[e]] - g[ra[e]]) * ((double)kb[j * D + cb[e]] - g[cb[e]]);
+  __shared__ double ga[32], gb[32];
+  if (t < 32) {
+    ga[t] = s1a / (double)M;
+    gb[t] = s1b / (double)M;
+    if (ai == bi) {
+      kglob[bh * D + 32 * ai + t] = (float)(s1a / (double)M);
+      kglob64[bh * D + 32 * ai + t] = s1a / (double)M;
+    }
   }
-  const int64_t BH = gridDim.x;
+  __syncthreads();
+  const int64_t BH = gridDim.x / (kT * kT);
+  const double inv_m = 1.0 / (double)M;
+  const double cv[2][2] = {{c00, c01}, {c10, c11}};
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const float c = (float)(acc[e] / (double)M);
-    const uint16_t h16 = f32_to_bf16_rne(c);
-    const float r1 = c - bits_f32((uint32_t)h16 << 16);
-    const uint16_t m16 = f32_to_bf16_rne(r1);
-    const uint16_t l16 = f32_to_bf16_rne(r1 - bits_f32((uint32_t)m16 << 16));
-    const int64_t off = (bh * D + ra[e]) * D + cb[e];
-    cp[0 * BH * D * D + off] = h16;
-    cp[1 * BH * D * D + off] = m16;
-    cp[2 * BH * D * D + off] = l16;
-  }
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      const int ra = 2 * ta + x, rb = 2 * tb + y;
+      const float c = (float)(cv[x][y] * inv_m - ga[ra] * gb[rb]);
+      const uint16_t h16 = f32_to_bf16_rne(c);
+      const float r1 = c - bits_f32((uint32_t)h16 << 16);
+      const uint16_t m16 = f32_to_bf16_rne(r1);
+      const uint16_t l16 = f32_to_bf16_rne(r1 - bits_f32((uint32_t)m16 << 16));
+      const int64_t off = (bh * D + 32 * ai + ra) * D + 32 * bi + rb;
+      cp[0 * BH * D * D + off] = h16;
+      cp[1 * BH * D * D + off] = m16;
+      cp[2 * BH * D * D + off] = l16;
+    }
 }
 
 hipError_t launch_pool(int d, int64_t BH, int64_t N, int block, const void* k, const void* v,
@@ -186,17 +196,12 @@ hipError_t launch_pool(int d, int64_t BH, int64_t N, int block, const void* k, c
 
 hipError_t launch_kstats(int d, int64_t BH, int64_t M, const float* kbar, float* kglob,
                          double* kglob64, uint16_t* cp, hipStream_t stream) {
-  if (d == 64) {
-    hipLaunchKernelGGL(kglob_kernel<64>, dim3((unsigned)BH), dim3(kThreads), 0, stream, kbar, M,
-                       kglob, kglob64);
-    hipLaunchKernelGGL(kcov_kernel<64>, dim3((unsigned)BH, 64 / 8), dim3(kThreads), 0, stream, kbar,
-                       M, kglob64, cp);
-  } else {
-    hipLaunchKernelGGL(kglob_kernel<128>, dim3((unsigned)BH), dim3(kThreads), 0, stream, kbar, M,
-                       kglob, kglob64);
-    hipLaunchKernelGGL(kcov_kernel<128>, dim3((unsigned)BH, 128 / 8), dim3(kThreads), 0, stream,
-                       kbar, M, kglob64, cp);
-  }
+  if (d == 64)
+    hipLaunchKernelGGL(kstats_kernel<64>, dim3((unsigned)(BH * 4)), dim3(kThreads), 0, stream,
+                       kbar, M, kglob, kglob64, cp);
+  else
+    hipLaunchKernelGGL(kstats_kernel<128>, dim3((unsigned)(BH * 16)), dim3(kThreads), 0, stream,
+                       kbar, M, kglob, kglob64, cp);
   return hipGetLastError();
 }
 
