@@ -178,7 +178,7 @@ int sol_attn_fwd_ex(const sol_shape* shape, const void* q, const void* k, const 
   uint16_t* kp = (uint16_t*)(ws + w.kp);
   uint16_t* vbt = (uint16_t*)(ws + w.vbt);
   float* tau = (float*)(ws + w.tau);
-  uint32_t* rowmask = (dbg && dbg->mask) ? dbg->mask : (uint32_t*)(ws + w.rowmask);
+  uint32_t* rowmask = (uint32_t*)(ws + w.rowmask);
   hipStream_t s = (hipStream_t)stream;
 
   auto mark = [&](int i) -> hipError_t {
@@ -218,6 +218,7 @@ int sol_attn_fwd_ex(const sol_shape* shape, const void* q, const void* k, const 
   a.vbt = vbt;
   a.tau = tau;
   a.rowmask = rowmask;
+  a.mask_out = dbg ? dbg->mask : nullptr;
   a.BH = BH;
   a.N = shape->N;
   a.M = M;

@@ -361,6 +361,134 @@ __device__ __forceinline__ void exact_stage(const lds_u8* ktile, const lds_u8* v
   for (int kb = 0; kb < NS; ++kb) pv32<D>(vtile, 32 * kb, pk[kb], o);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Software-pipelined exact loop, in steps of 32 keys (half a 64-key stage).  A wave keeps two
+// score blocks live: while the matrix cores compute S^T of the next 32 keys (phase A), the vector
+// ALU turns the current 32 keys' scores into probabilities; while the matrix cores accumulate
+// O^T += V^T P^T for the current 32 keys (phase B), the vector ALU takes the next block's row
+// maximum.  K and V tiles are double buffered separately, each with its own barrier, so the next
+// stage's keys can be in use while this stage's values still are.  Instruction groups are
+// interleaved with sched_group_barrier so that every MFMA has independent vector work behind it.
+// ---------------------------------------------------------------------------------------------
+constexpr int kSgMfma = 0x008, kSgValu = 0x002 | 0x400, kSgDsRead = 0x100;
+
+// Phase A: (QK) sn = S^T of the 32 keys at rows kr0.. of ktile, and the probabilities of the
+// current block sc (offset moff = -running max, or -inf for rows that do not take part) packed
+// into pk, with their rounded sum added to ps.
+template <int D, bool QK>
+__device__ __forceinline__ void phase_a(const lds_u8* ktile, int kr0, const bf16x8 (&qf)[D / 16],
+                                        f32x16& sn, const f32x16& sc, float sl2, float moff,
+                                        uint32_t (&pk)[8], float& ps) {
+  constexpr int NM = D / 16;        // MFMAs
+  constexpr int PER = 16 / NM;      // probabilities per MFMA slot (even)
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 31, h = lane >> 5;
+  if constexpr (QK) sn = f32x16{};
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    if constexpr (QK) {
+      const u32x4 raw = lds_read16(ktile + tile_off<D>(kr0 + c, 2 * i + h));
+      sn = mfma32(__builtin_bit_cast(bf16x8, raw), qf[i], sn);
+    }
+#pragma unroll
+    for (int u = 0; u < PER; u += 2) {
+      const int v = i * PER + u;
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[v], sl2, moff));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[v + 1], sl2, moff));
+      pk[v / 2] = pack_bf16x2(p0, p1);
+      ps = add_bf16x2(pk[v / 2], ps);
+    }
+  }
+  if constexpr (QK) {
+    // K operand reads run three MFMAs ahead
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 3, 0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i + 3 < NM) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgValu, 3 * PER, 0);
+    }
+  }
+}
+
+// Phase B: O^T += V^T P^T for the 32 keys at rows vr0.. of vtile and, when MX, the maximum of the
+// next block's scores sn (raw, before scaling).
+template <int D, bool MX>
+__device__ __forceinline__ float phase_b(const lds_u8* vtile, int vr0, const uint32_t (&pk)[8],
+                                         const f32x16& sn, f32x16 (&o)[D / 32]) {
+  constexpr int NM = 2 * (D / 32);  // MFMAs
+  constexpr int PER = 16 / NM;      // maxima per MFMA slot
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4, j = lane & 15;
+  const int h = grp >> 1, cg = grp & 1;
+  float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+  for (int e2 = 0; e2 < 2; ++e2) {
+    const bf16x8 b = p_operand(pk, e2);
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds) {
+      const int d0 = 32 * ds + 16 * cg + 4 * (j & 3);
+      s16x4 x[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int row = vr0 + 16 * e2 + 8 * r + 4 * h + (j >> 2);
+        const lds_u8* p = vtile + tile_off<D>(row, d0 >> 3) + ((d0 >> 2) & 1) * 8;
+        x[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(p));
+      }
+      u32x4 raw;
+      raw[0] = __builtin_bit_cast(u32x2, x[0])[0];
+      raw[1] = __builtin_bit_cast(u32x2, x[0])[1];
+      raw[2] = __builtin_bit_cast(u32x2, x[1])[0];
+      raw[3] = __builtin_bit_cast(u32x2, x[1])[1];
+      o[ds] = mfma32(__builtin_bit_cast(bf16x8, raw), b, o[ds]);
+      if constexpr (MX) {
+        const int step = e2 * (D / 32) + ds;
+#pragma unroll
+        for (int u = 0; u < PER; u += 2) {
+          m0 = fmaxf(m0, sn[step * PER + u]);
+          m1 = fmaxf(m1, sn[step * PER + u + 1]);
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    if (i + 2 < NM) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    if constexpr (MX) __builtin_amdgcn_sched_group_barrier(kSgValu, PER, 0);
+  }
+  return fmaxf(m0, m1);
+}
+
+// Keys of a 32-key block at or beyond nvalid (counted from the block's first key) get -inf.
+__device__ __forceinline__ void mask_tail(f32x16& s, int nvalid) {
+  const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+    if (key_of(v, h) >= nvalid) s[v] = -INFINITY;
+}
+
+// Raise the running max to the block maximum mt_raw (raw score units) when it exceeds it by more
+// than kSlack, rescaling the accumulators; rows that do not take part never raise it.
+template <int D>
+__device__ __forceinline__ void raise_max(float mt_raw, bool active, float sl2, float& mrun,
+                                          float& lsum, f32x16 (&o)[D / 32]) {
+  const float mt = pair_max(mt_raw) * sl2;
+  const bool grow = active && mt > mrun + kSlack;
+  if (__builtin_amdgcn_ballot_w64(grow)) {
+    const float mnew = grow ? mt : mrun;
+    const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+    mrun = mnew;
+    lsum *= alpha;
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[ds][v] *= alpha;
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void load_q(const uint16_t* __restrict__ qrow, bool valid,
                                        bf16x8 (&qf)[D / 16]) {
@@ -542,7 +670,7 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
   const uint16_t* qb = a.q + bh * a.N * D;
   const uint16_t* kb = a.k + bh * a.N * D;
   const uint16_t* vb = a.v + bh * a.N * D;
-  uint32_t* rmask = a.rowmask + (bh * a.N) * W;
+  uint32_t* rmask = a.rowmask + bh * W * a.N;  // word w of row r at rmask[w * N + r]
 
   bf16x8 qf[D / 16];
   load_q<D>(qb + row * D, rvalid, qf);
@@ -613,7 +741,10 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
       }
     }
     const uint32_t word = pair_or(bits);
-    if (h == 0 && rvalid) rmask[row * W + cb] = word;
+    if (h == 0 && rvalid) {
+      rmask[(int64_t)cb * a.N + row] = word;
+      if (a.mask_out) a.mask_out[(bh * a.N + row) * W + cb] = word;
+    }
     // tile union: one LDS atomic OR per row (no dependent cross-lane reduction)
     if (h == 0 && word) atomicOr(&umask[cb], word);
     if (!a.drop) {
@@ -673,25 +804,38 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
   };
 
   // One barrier per stage: it publishes the stage's copy (each lane waited for its own loads)
-  // and retires the previous stage's reads, so the next copy can go into that buffer.
+  // and retires the previous stage's reads, so the next copy can go into that buffer.  A row's
+  // selection word for the next stage's block is loaded together with that stage's copy, so the
+  // wait at the top of the loop covers it.
+  auto load_word = [&](int wd) -> uint32_t {
+    return rvalid ? rmask[(int64_t)wd * a.N + row] : 0u;
+  };
   int kept_blocks = 0;
   int cur_j = -1, cur_s = 0;
   bool have = next_stage(cur_j, cur_s);
-  if (have) issue(cur_j, cur_s, 0);
-  int buf = 0;
   int mask_w = -1;
   uint32_t mask_word = 0u;
+  if (have) {
+    issue(cur_j, cur_s, 0);
+    mask_w = cur_j >> 5;
+    mask_word = load_word(mask_w);
+  }
+  int buf = 0;
   while (have) {
     wait_vmcnt<0>();
     bar();
     int nj = -1, ns = 0;
     const bool more = next_stage(nj, ns);
-    if (more) issue(nj, ns, buf ^ 1);
-    if (cur_s == 0) ++kept_blocks;
-    if ((cur_j >> 5) != mask_w) {
-      mask_w = cur_j >> 5;
-      mask_word = rvalid ? rmask[row * W + mask_w] : 0u;
+    int next_w = mask_w;
+    uint32_t next_word = mask_word;
+    if (more) {
+      issue(nj, ns, buf ^ 1);
+      if ((nj >> 5) != mask_w) {
+        next_w = nj >> 5;
+        next_word = load_word(next_w);
+      }
     }
+    if (cur_s == 0) ++kept_blocks;
     const bool active = (mask_word >> (cur_j & 31)) & 1u;
     const int r0 = cur_j * BLK + cur_s * kStage;
     const int nvalid = (int)a.N - r0 < kStage ? (int)a.N - r0 : kStage;
@@ -700,6 +844,8 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
     buf ^= 1;
     cur_j = nj;
     cur_s = ns;
+    mask_w = next_w;
+    mask_word = next_word;
     have = more;
   }
   if (a.tile_kept && t == 0) a.tile_kept[bh * ntiles + tile] = kept_blocks;
@@ -708,6 +854,56 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
   epilogue<D>(o, mrun, lsum, row0, a.N, a.out + bh * a.N * D,
               a.out_f32 ? a.out_f32 + bh * a.N * D : nullptr, a.lse ? a.lse + bh * a.N : nullptr,
               smem + wave * 32 * D * 2);
+}
+
+// Half HB of stage n of the pipelined exact loop over consecutive stages (dense kernel); B = n & 1.
+// NEXT: a next 32-key block exists (it may be partial).  sc holds the current block's scores,
+// sn receives the next block's.  K tiles live at kbuf + b * tile, V tiles at vbuf + b * tile.
+// Copies are issued K0, V0, K1 (prologue), then V_{n+1} at half 0 and K_{n+2} at half 1 of stage n.
+template <int D, int B, int HB, bool NEXT>
+__device__ __forceinline__ void dense_half(int n, int nst, int64_t N, const uint16_t* kb,
+                                           const uint16_t* vb, lds_u8* kbuf, lds_u8* vbuf,
+                                           const TileOffsets<D, kStage>& toff,
+                                           const bf16x8 (&qf)[D / 16], float sl2,
+                                           const f32x16& sc, f32x16& sn, float& mrun,
+                                           float& lsum, f32x16 (&o)[D / 32]) {
+  constexpr int kTileBytes = kStage * D * 2;
+  constexpr int L = tile_loads<D, kStage>();
+  auto issue = [&](const uint16_t* src, int st, lds_u8* dst) {
+    const int r0 = st * kStage;
+    const uint32_t bytes = (uint32_t)((int)N - r0) * (uint32_t)(D * 2);
+    load_tile_buf<D, kStage>(make_rsrc(src + (int64_t)r0 * D, bytes), 0u, toff, dst);
+  };
+  const bool more = n + 1 < nst;
+  if constexpr (HB == 0) {
+    // V_n has landed (only K_{n+1}, issued after it, may be in flight); after the barrier every
+    // wave is done with V_{n-1}, whose buffer takes V_{n+1}
+    if (more) wait_vmcnt<L>();
+    else wait_vmcnt<0>();
+    bar();
+    if (more) issue(vb, n + 1, vbuf + (B ^ 1) * kTileBytes);
+  } else {
+    // K_{n+1} has landed (only V_{n+1} may be in flight); after the barrier every wave is done
+    // with K_n, whose buffer takes K_{n+2}
+    if (more) wait_vmcnt<L>();
+    bar();
+    if (n + 2 < nst) issue(kb, n + 2, kbuf + B * kTileBytes);
+  }
+  uint32_t pk[8];
+  float ps = 0.f;
+  const lds_u8* knext = HB == 0 ? kbuf + B * kTileBytes : kbuf + (B ^ 1) * kTileBytes;
+  phase_a<D, NEXT>(knext, HB == 0 ? 32 : 0, qf, sn, sc, sl2, -mrun, pk, ps);
+  if constexpr (NEXT) {
+    const int nv = (int)(N - (int64_t)n * kStage) - (HB == 0 ? 32 : 64);
+    if (nv < 32) mask_tail(sn, nv);
+  }
+  lsum += ps;
+  if constexpr (NEXT) {
+    const float mt = phase_b<D, true>(vbuf + B * kTileBytes, 32 * HB, pk, sn, o);
+    raise_max<D>(mt, true, sl2, mrun, lsum, o);
+  } else {
+    phase_b<D, false>(vbuf + B * kTileBytes, 32 * HB, pk, sn, o);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -724,7 +920,6 @@ __global__ __launch_bounds__(kThreads, 2) void dense_attn_kernel(const uint16_t*
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   lds_u8* smem = (lds_u8*)smem_raw;
   constexpr int kTileBytes = kStage * D * 2;
-  constexpr int kStageBytes = 2 * kTileBytes;
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, c = lane & 31;
   const int64_t ntiles = (N + kQTile - 1) / kQTile;
@@ -748,23 +943,45 @@ __global__ __launch_bounds__(kThreads, 2) void dense_attn_kernel(const uint16_t*
 
   const int nst = (int)((N + kStage - 1) / kStage);
   const TileOffsets<D, kStage> toff;
-  auto issue = [&](int st, lds_u8* base) {
+  lds_u8* kbuf = smem;                        // K tiles: kbuf + b * kTileBytes
+  lds_u8* vbuf = smem + 2 * kTileBytes;       // V tiles
+  auto issue = [&](const uint16_t* src, int st, lds_u8* dst) {
     const int r0 = st * kStage;
     const uint32_t bytes = (uint32_t)((int)N - r0) * (uint32_t)(D * 2);
-    load_tile_buf<D, kStage>(make_rsrc(kb + (int64_t)r0 * D, bytes), 0u, toff, base);
-    load_tile_buf<D, kStage>(make_rsrc(vb + (int64_t)r0 * D, bytes), 0u, toff, base + kTileBytes);
+    load_tile_buf<D, kStage>(make_rsrc(src + (int64_t)r0 * D, bytes), 0u, toff, dst);
   };
-  issue(0, smem);
-  int buf = 0;
-  for (int st = 0; st < nst; ++st) {
-    wait_vmcnt<0>();
-    bar();  // publishes stage st, retires stage st - 1's buffer
-    if (st + 1 < nst) issue(st + 1, smem + (buf ^ 1) * kStageBytes);
-    const int r0 = st * kStage;
-    const int nvalid = (int)N - r0 < kStage ? (int)N - r0 : kStage;
-    const lds_u8* base = smem + buf * kStageBytes;
-    exact_stage<D>(base, base + kTileBytes, qf, true, nvalid, sl2, mrun, lsum, o);
-    buf ^= 1;
+
+  // prologue: K0, V0, K1 in LDS; scores and max of the first 32 keys
+  issue(kb, 0, kbuf);
+  issue(vb, 0, vbuf);
+  if (nst > 1) issue(kb, 1, kbuf + kTileBytes);
+  wait_vmcnt<0>();
+  bar();
+  f32x16 sa = scores32<D>(kbuf, 0, qf, f32x16{}), sb;
+  if (N < 32) mask_tail(sa, (int)N);
+  {
+    float m = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) m = fmaxf(m, sa[v]);
+    mrun = pair_max(m) * sl2;
+  }
+  // stages n (buffers 0) and n + 1 (buffers 1) per iteration; the last stage's half 1 has no
+  // next block
+  int n = 0;
+  for (; n + 2 < nst; n += 2) {
+    dense_half<D, 0, 0, true>(n, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
+    dense_half<D, 0, 1, true>(n, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
+    dense_half<D, 1, 0, true>(n + 1, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
+    dense_half<D, 1, 1, true>(n + 1, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
+  }
+  if (n + 1 < nst) {
+    dense_half<D, 0, 0, true>(n, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
+    dense_half<D, 0, 1, true>(n, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
+    dense_half<D, 1, 0, true>(n + 1, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
+    dense_half<D, 1, 1, false>(n + 1, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
+  } else {
+    dense_half<D, 0, 0, true>(n, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
+    dense_half<D, 0, 1, false>(n, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
   }
   bar();  // stage buffers free for the epilogue
   epilogue<D>(o, mrun, lsum, row0, N, out + bh * N * D, nullptr, lse ? lse + bh * N : nullptr,

@@ -36,11 +36,13 @@ struct SparseArgs {
   const uint16_t* kp;   // [3][BH][Mp][d] pooled keys (hi, mid, lo)
   const uint16_t* vbt;  // [BH][d][Mp] pooled values, transposed
   const float* tau;     // [BH][N]
-  uint32_t* rowmask;    // [BH][N][Mp/32] selection words (written, then read back per row)
+  uint32_t* rowmask;    // [BH][Mp/32][N] selection words, word-major (written by the routing
+                        // sweep, read back per row by the exact loop)
   int64_t BH, N, M, Mp;
   int block;
   int drop;
   // optional outputs
+  uint32_t* mask_out;   // [BH][N][Mp/32] selection words, row-major
   float* lse;
   int32_t* tile_kept;
   float* out_f32;
