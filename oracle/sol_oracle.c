@@ -23,6 +23,10 @@
  *   beta        -inf keeps every block, +inf keeps none (even when sigma_i = 0); NaN is an error.
  *   blocks      contiguous runs of the flattened token order; the last block may be partial.
  *
+ * Parity unpinned: whether this pooled-token form is the paper's own correction term.  The page
+ * does not print that term, so no value on it can pin the choice; every other function here is
+ * pinned by the tests (hand examples, limits, special cases and invariants).
+ *
  * Everything is fp64.  Inputs are fp32 arrays that hold bf16 values exactly.  The code follows
  * the definition step by step, one query row at a time, with no blocking, fusion or reordering.
  * OpenMP splits rows across threads; each row is computed independently in a fixed order, so the
