@@ -192,12 +192,15 @@ def main():
     kept_blocks = int(dbg["tile_kept"].sum().item())
     rho_tile = kept_blocks / (B * H * T * M)
     F_tile = sol.kept_block_flops(dbg["tile_kept"], dbg["mask"], N, d, w.block)
+    units = sol.union_units(dbg["mask"], N, w.block)
+    F_row, F_exec = 4.0 * d * units[1], 4.0 * d * units[32]
     mask = dbg["mask"].view(torch.int32)
     row_bits = sum(int(torch.bitwise_and(torch.bitwise_right_shift(mask, s), 1).sum().item())
                    for s in range(32))
     rho_row = row_bits / (B * H * N * M)
-    del dbg
-    log(f"beta={beta:.4f} rho_tile={rho_tile:.4f} rho_row={rho_row:.4f} F_tile={F_tile / 1e12:.2f} TF")
+    del dbg, mask
+    log(f"beta={beta:.4f} rho_tile={rho_tile:.4f} rho_row={rho_row:.4f} F_tile={F_tile / 1e12:.2f} TF "
+        f"F_exec={F_exec / 1e12:.2f} TF F_row={F_row / 1e12:.2f} TF")
 
     K, Wm = args.steps, args.warmup
     ev = sol.HipEvents(4 * (K + Wm))
@@ -232,7 +235,10 @@ def main():
 
     dense_F = sol.dense_flops(B, H, N, d)
     pool_bytes = 2 * B * H * N * d * 2 + 2 * B * H * M * d * 4  # K,V read + Kbar,Vbar (fp32) written
+    # algorithmic work: 4*d FLOPs per (row, key) of every kept (128-row tile, block) pair; the
+    # matrix cores skip, per 32-row wave, blocks none of its rows keeps, so they execute F_exec
     achieved = F_tile / (t_fused * 1e-3) / 1e12
+    executed = F_exec / (t_fused * 1e-3) / 1e12
     result = {
         "metric": METRIC,
         "value": F_tile / (t_sparse * 1e-3) / 1e12,
@@ -263,6 +269,10 @@ def main():
         "rho_tile": rho_tile,
         "rho_row": rho_row,
         "kept_block_tflop": F_tile / 1e12,
+        "executed_block_tflop": F_exec / 1e12,
+        "row_kept_tflop": F_row / 1e12,
+        "fused_executed_tflops": executed,
+        "fused_executed_mfma_frac": executed / PEAK_BF16_TFLOPS,
         "pool_gbs": pool_bytes / (t_pool * 1e-3) / 1e9,
         "roofline": {
             "bound": "mfma",
@@ -274,6 +284,8 @@ def main():
                 [os.path.join(ROOT, "block_sparse_attention_sol_amd", "csrc", f)
                  for f in ("attn.hip", "common.hpp", "kernels.hpp")], w.name, beta),
             "kernel": "sol_attn_kernel<128,128> (fused routing + pooled tokens + exact attention)",
+            "flops": "kept-block FLOPs F_tile: 4*d per (row, key) of each block some row of the "
+                     "row's 128-row query tile keeps",
         },
     }
     if not args.no_cpu_baseline:

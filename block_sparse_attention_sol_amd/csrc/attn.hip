@@ -840,7 +840,10 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
     const int r0 = cur_j * BLK + cur_s * kStage;
     const int nvalid = (int)a.N - r0 < kStage ? (int)a.N - r0 : kStage;
     const lds_u8* base = smem + buf * kStageBytes;
-    exact_stage<D>(base, base + kTileBytes, qf, active, nvalid, sl2, mrun, lsum, o);
+    // a wave none of whose rows keeps the block has nothing to add (every probability would be
+    // 0): it skips the stage's math and only takes part in the copies and barriers
+    if (__builtin_amdgcn_ballot_w64(active))
+      exact_stage<D>(base, base + kTileBytes, qf, active, nvalid, sl2, mrun, lsum, o);
     buf ^= 1;
     cur_j = nj;
     cur_s = ns;

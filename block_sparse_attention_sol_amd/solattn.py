@@ -229,6 +229,37 @@ def kept_block_flops(tile_kept, mask, N: int, d: int, block: int) -> float:
     return float(4.0 * d * units)
 
 
+def union_units(mask, N: int, block: int, heights=(1, 32, QUERY_TILE)) -> dict:
+    """Computed (query row, key) pairs when a key block is computed for a group of `height`
+    consecutive query rows whenever any row of the group keeps it: for each height,
+    sum over groups g of sum over blocks j kept by some row of g of rows_g * n_j.
+
+    Height 1 is the per-row selection itself, 32 the rows of one wave (a wave skips blocks none
+    of its rows keeps), 128 the query tile.  mask [B, H, N, W] is the kernel's debug output.
+    Returns {height: units}; FLOPs are 4 * d * units."""
+    import torch
+    B, H = mask.shape[0], mask.shape[1]
+    M = n_blocks(N, block)
+    dev = mask.device
+    n = torch.full((M,), float(block), dtype=torch.float64, device=dev)
+    n[-1] = float(N - (M - 1) * block)
+    shifts = torch.arange(32, device=dev, dtype=torch.int32)
+    out = {hgt: 0.0 for hgt in heights}
+    for b in range(B):
+        for h in range(H):
+            bits = ((mask[b, h].view(torch.int32).unsqueeze(-1) >> shifts) & 1).to(torch.uint8)
+            bits = bits.reshape(N, -1)[:, :M]                                  # [N, M]
+            for hgt in heights:
+                G = (N + hgt - 1) // hgt
+                padded = torch.nn.functional.pad(bits, (0, 0, 0, G * hgt - N))
+                u = padded.view(G, hgt, M).amax(dim=1).to(torch.float64)       # [G, M]
+                rows = torch.full((G,), float(hgt), dtype=torch.float64, device=dev)
+                rows[-1] = float(N - (G - 1) * hgt)
+                out[hgt] += float((rows[:, None] * u * n[None, :]).sum())
+            del bits
+    return out
+
+
 def dense_flops(B: int, H: int, N: int, d: int) -> float:
     return 4.0 * B * H * N * N * d
 
