@@ -35,23 +35,31 @@ def log(msg: str):
     print(msg, file=sys.stderr, flush=True)
 
 
-def calibrate_beta(sol, q, k, v, block, target, ws, out):
-    """Bisection on beta so that the kept-block density at query-tile granularity hits target
-    (density is non-increasing in beta)."""
+def calibrate_beta(sol, q, k, v, block, target, ws, out, per_row=False):
+    """Bisection on beta so that the kept-block density hits target (density is non-increasing in
+    beta): at query-tile granularity (rho_tile), or per row (rho_row) when per_row is set."""
     import torch
-    M = sol.n_blocks(q.shape[2], block)
+    N = q.shape[2]
+    M = sol.n_blocks(N, block)
 
     def density(beta):
         _, dbg = sol.attn_fwd(q, k, v, beta, block, out=out, workspace=ws, debug=True)
+        if per_row:
+            mask = dbg["mask"].view(torch.int32)
+            bits = sum(int(torch.bitwise_and(torch.bitwise_right_shift(mask, s), 1).sum().item())
+                       for s in range(32))
+            return bits / (q.shape[0] * q.shape[1] * N * M)
         tk = dbg["tile_kept"]
         return float(tk.sum().item()) / (tk.numel() * M)
 
     lo, hi = 0.0, 4.0
-    d_lo, d_hi = density(lo), density(hi)
+    d_hi = density(hi)
     while d_hi > target and hi < 16:
         lo, hi = hi, hi * 2
         d_hi = density(hi)
-    for _ in range(18):
+    if density(lo) < target:
+        lo = -8.0
+    for _ in range(20):
         mid = 0.5 * (lo + hi)
         dm = density(mid)
         if dm > target:
@@ -62,6 +70,22 @@ def calibrate_beta(sol, q, k, v, block, target, ws, out):
             return mid
     torch.cuda.synchronize()
     return 0.5 * (lo + hi)
+
+
+def mfma_probe_tflops(sol, workgroups=2048, iters=1000, reps=3):
+    """bf16 MFMA rate of the library's matrix-core probe (best of reps), TFLOP/s."""
+    import torch
+    sink, flops = sol.mfma_probe(workgroups, iters)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        sol.mfma_probe(workgroups, iters, sink=sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return best
 
 
 def cpu_baseline(w, q, k, v, beta, F_tile, seconds=12.0):
@@ -142,6 +166,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan")
     ap.add_argument("--beta", type=float, default=None)
+    ap.add_argument("--target", type=float, default=None,
+                    help="kept-block density (at 128-row query tiles) to calibrate beta to, instead "
+                         "of the workload's own target")
+    ap.add_argument("--row-target", type=float, default=None,
+                    help="calibrate beta to this per-row kept density instead (the secondary "
+                         "operating point)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (calibrates the HBM "
@@ -172,8 +202,16 @@ def main():
     sol.load_library()
     w = synth.WORKLOADS[args.workload]
     target = w.target_density[0] if w.target_density else None
+    if args.target is not None:
+        target = args.target
     log(f"workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} block={w.block}; generating")
-    q, k, v = (t.cuda() for t in synth.generate(w))
+    t0 = time.perf_counter()
+
+    def gen_progress(b, h):
+        if (h + 1) % 8 == 0 or h + 1 == w.H:
+            log(f"  generated head {h + 1}/{w.H} ({time.perf_counter() - t0:.0f} s)")
+
+    q, k, v = (t.cuda() for t in synth.generate(w, progress=gen_progress))
     B, H, N, d = q.shape
     out = torch.empty_like(q)
     dout = torch.empty_like(q)
@@ -181,6 +219,8 @@ def main():
 
     if args.beta is not None:
         beta = args.beta
+    elif args.row_target is not None:
+        beta = calibrate_beta(sol, q, k, v, w.block, args.row_target, ws, out, per_row=True)
     elif target is not None:
         beta = calibrate_beta(sol, q, k, v, w.block, target, ws, out)
     else:
@@ -201,6 +241,9 @@ def main():
     del dbg, mask
     log(f"beta={beta:.4f} rho_tile={rho_tile:.4f} rho_row={rho_row:.4f} F_tile={F_tile / 1e12:.2f} TF "
         f"F_exec={F_exec / 1e12:.2f} TF F_row={F_row / 1e12:.2f} TF")
+
+    probe = mfma_probe_tflops(sol)
+    log(f"matrix-core probe: {probe:.0f} TFLOP/s bf16")
 
     K, Wm = args.steps, args.warmup
     ev = sol.HipEvents(4 * (K + Wm))
@@ -256,7 +299,8 @@ def main():
             "workload": f"{w.name}: {w.grid[0]}x{w.grid[1]}x{w.grid[2]} latent grid, positional amplitude "
                         f"{w.amp_range or w.amp}, seed 0",
             "B": B, "H": H, "N": N, "d": d, "block": w.block, "beta": round(beta, 5),
-            "target_kept_block_density": target, "query_tile": sol.QUERY_TILE,
+            "target_kept_block_density": None if args.row_target is not None else target,
+            "target_row_density": args.row_target, "query_tile": sol.QUERY_TILE,
             "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)",
         },
         "sparse_ms": t_sparse,
@@ -265,6 +309,8 @@ def main():
         "speedup_vs_dense": t_dense / t_sparse,
         "dense_tflops": dense_F / (t_dense * 1e-3) / 1e12,
         "dense_mfma_frac": dense_F / (t_dense * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "dense_frac_of_measured_peak": dense_F / (t_dense * 1e-3) / 1e12 / probe,
+        "mfma_probe_tflops": probe,
         "kernel_ms": {"pool_kv": t_pool, "row_stats": avg(kglob_ms), "fused": t_fused},
         "rho_tile": rho_tile,
         "rho_row": rho_row,
@@ -280,6 +326,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
+            "measured_peak": probe,
+            "frac_of_measured_peak": achieved / probe,
             "traffic": recorded_traffic(
                 [os.path.join(ROOT, "block_sparse_attention_sol_amd", "csrc", f)
                  for f in ("attn.hip", "common.hpp", "kernels.hpp")], w.name, beta),

@@ -103,6 +103,15 @@ int hip_status(hipError_t e, const char* what) {
 
 extern "C" {
 
+int sol_mfma_probe(int workgroups, int iters, float* sink, void* stream) {
+  if (workgroups < 1) return fail(SOL_EINVAL, "workgroups must be >= 1 (got %d)", workgroups);
+  if (iters < 1) return fail(SOL_EINVAL, "iters must be >= 1 (got %d)", iters);
+  if (!sink) return fail(SOL_EINVAL, "sink is NULL");
+  const hipError_t e = solattn::launch_mfma_probe(workgroups, iters, sink, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SOL_EHIP, "mfma probe launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* sol_version(void) { return "libsolattn 0.1 (gfx950)"; }
 
 const char* sol_status_str(int status) {

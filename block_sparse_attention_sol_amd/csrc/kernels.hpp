@@ -52,4 +52,9 @@ hipError_t launch_sparse(int d, const SparseArgs& a, hipStream_t stream);
 hipError_t launch_dense(int d, int64_t BH, int64_t N, const void* q, const void* k, const void* v,
                         void* out, float* lse, hipStream_t stream);
 
+// Matrix-core rate probe: `workgroups` x 4 waves, each issuing iters x mfma_probe_chains()
+// independent bf16 32x32x16 MFMAs.
+hipError_t launch_mfma_probe(int workgroups, int iters, float* sink, hipStream_t stream);
+int mfma_probe_chains();
+
 }  // namespace solattn

@@ -26,6 +26,7 @@ EXPORTS = (
     "sol_pool_kv",
     "sol_attn_fwd",
     "sol_attn_fwd_ex",
+    "sol_mfma_probe",
     "sol_dense_fwd",
     "sol_status_str",
     "sol_last_error",
@@ -74,7 +75,8 @@ def load_library(path: str = LIB_PATH):
     lib.sol_attn_fwd_ex.argtypes = [shp, vp, vp, vp, cf, ci, vp, vp, sz,
                                     ctypes.POINTER(SolAttnDebug), vp]
     lib.sol_dense_fwd.argtypes = [shp, vp, vp, vp, vp, vp, vp]
-    for f in ("sol_pool_kv", "sol_attn_fwd", "sol_attn_fwd_ex", "sol_dense_fwd"):
+    lib.sol_mfma_probe.argtypes = [ci, ci, vp, vp]
+    for f in ("sol_pool_kv", "sol_attn_fwd", "sol_attn_fwd_ex", "sol_dense_fwd", "sol_mfma_probe"):
         getattr(lib, f).restype = ci
     lib.sol_status_str.argtypes = [ci]
     lib.sol_status_str.restype = ctypes.c_char_p
@@ -205,6 +207,19 @@ def dense_fwd(q, k, v, out=None, want_lse: bool = False, stream=None):
                              _dev(out, "out"), _dev(lse, "lse") if lse is not None else None,
                              _stream(stream)))
     return (out, lse) if want_lse else out
+
+
+MFMA_PROBE_FLOPS_PER_WAVE_ITER = 8 * 32768  # 8 independent 32x32x16 bf16 MFMAs
+
+
+def mfma_probe(workgroups: int, iters: int, sink=None, stream=None):
+    """Launch the matrix-core rate probe; returns (sink, FLOPs issued).  Time it with events."""
+    import torch
+    lib = load_library()
+    if sink is None:
+        sink = torch.empty(workgroups, dtype=torch.float32, device="cuda")
+    _check(lib.sol_mfma_probe(int(workgroups), int(iters), _dev(sink, "sink"), _stream(stream)))
+    return sink, float(workgroups) * 4 * iters * MFMA_PROBE_FLOPS_PER_WAVE_ITER
 
 
 def kept_block_flops(tile_kept, mask, N: int, d: int, block: int) -> float:

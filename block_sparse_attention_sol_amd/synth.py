@@ -101,11 +101,13 @@ def amplitudes(w: Workload, rng: np.random.Generator) -> np.ndarray:
     return np.full(w.H, w.amp)
 
 
-def generate(w: Workload | str, seed: int = 0, heads: int | None = None, keep_fp32: bool = False):
+def generate(w: Workload | str, seed: int = 0, heads: int | None = None, keep_fp32: bool = False,
+             progress=None):
     """Q, K, V as bf16 torch CPU tensors [B, H, N, d] (contiguous).
 
     heads: generate only the first `heads` heads (the draw sequence of those heads is identical
-    to a full generation).  keep_fp32: also return the fp32 arrays before rounding."""
+    to a full generation).  keep_fp32: also return the fp32 arrays before rounding.
+    progress: optional callable(b, h) invoked after each head is generated."""
     import torch
 
     if isinstance(w, str):
@@ -123,6 +125,8 @@ def generate(w: Workload | str, seed: int = 0, heads: int | None = None, keep_fp
                 out[i][b, h].copy_(torch.from_numpy(a).to(torch.bfloat16))
                 if keep_fp32:
                     masters[i][b, h] = a
+            if progress is not None:
+                progress(b, h)
     if keep_fp32:
         return out[0], out[1], out[2], masters
     return out[0], out[1], out[2]

@@ -119,6 +119,17 @@ int sol_attn_fwd_ex(const sol_shape* shape, const void* q, const void* k, const 
 int sol_dense_fwd(const sol_shape* shape, const void* q, const void* k, const void* v, void* out,
                   float* lse, void* stream);
 
+/*
+ * Matrix-core rate probe (measurement only, not part of the attention path): `workgroups`
+ * workgroups of 4 waves each issue iters x 8 independent bf16 32x32x16 MFMAs (32768 FLOPs each)
+ * on register operands, so FLOPs = workgroups * 4 * iters * 8 * 32768.  sink (device,
+ * [workgroups] fp32, written) receives one value per workgroup so that no work is optimised away.
+ * Timed by the caller (e.g. with events on `stream`), it gives the bf16 MFMA rate this part
+ * sustains, against which the attention kernels' rates are also reported.
+ * Errors: SOL_EINVAL for workgroups < 1, iters < 1 or a NULL sink; SOL_EHIP if the launch fails.
+ */
+int sol_mfma_probe(int workgroups, int iters, float* sink, void* stream);
+
 /* Static text for a status code. */
 const char* sol_status_str(int status);
 /* Message for the last error returned on the calling thread ("" if none). */

@@ -157,3 +157,11 @@ def test_binding_refuses_cpu_tensors(lib):
     with pytest.raises(ValueError):
         solattn.attn_fwd(q, q, q, 0.5, 64, out=torch.zeros_like(q),
                          workspace=torch.zeros(1 << 20, dtype=torch.uint8))
+
+
+def test_mfma_probe_rejects(lib):
+    sink = _ptrs(1)[0]
+    assert lib.sol_mfma_probe(0, 10, sink, None) == solattn.SOL_EINVAL
+    assert lib.sol_mfma_probe(8, 0, sink, None) == solattn.SOL_EINVAL
+    assert lib.sol_mfma_probe(8, 10, None, None) == solattn.SOL_EINVAL
+    assert b"sink" in lib.sol_last_error()
