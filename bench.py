@@ -173,6 +173,8 @@ def main():
                     help="calibrate beta to this per-row kept density instead (the secondary "
                          "operating point)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cache", default=None, metavar="DIR",
+                    help="keep the generated inputs in DIR (torch.save) and reuse them on later runs")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (calibrates the HBM "
                          "byte counters of a profiler run) and exit")
@@ -211,7 +213,17 @@ def main():
         if (h + 1) % 8 == 0 or h + 1 == w.H:
             log(f"  generated head {h + 1}/{w.H} ({time.perf_counter() - t0:.0f} s)")
 
-    q, k, v = (t.cuda() for t in synth.generate(w, progress=gen_progress))
+    cache = os.path.join(args.cache, f"{w.name}_seed0.pt") if args.cache else None
+    if cache and os.path.exists(cache):
+        q, k, v = (t.cuda() for t in torch.load(cache, weights_only=True))
+        log(f"  loaded inputs from {cache}")
+    else:
+        qkv = synth.generate(w, progress=gen_progress)
+        if cache:
+            os.makedirs(args.cache, exist_ok=True)
+            torch.save(list(qkv), cache)
+        q, k, v = (t.cuda() for t in qkv)
+        del qkv
     B, H, N, d = q.shape
     out = torch.empty_like(q)
     dout = torch.empty_like(q)
