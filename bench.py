@@ -137,6 +137,66 @@ def cpu_baseline(w, q, k, v, beta, F_tile, seconds=12.0):
     }
 
 
+def ablation(sol, w, q, k, v, ws, betas, rows_per_head=48, steps=5):
+    """Drop-vs-approximate ablation: for each beta, the output of the method (unselected blocks as
+    pooled tokens) and of the same selection with unselected blocks dropped, both against exact
+    dense softmax attention computed by the fp64 oracle on seeded sampled rows of every head;
+    plus the fused kernel's time in each mode."""
+    import numpy as np
+    import torch
+    from oracle import oracle
+    B, H, N, d = q.shape
+    rng = np.random.default_rng(1)
+    rows = [np.sort(rng.choice(N, size=min(rows_per_head, N), replace=False)) for _ in range(B * H)]
+    ref = []
+    t0 = time.perf_counter()
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        qh, kh, vh = (t[b, h].float().cpu().numpy() for t in (q, k, v))
+        ref.append(oracle.dense_rows(qh, kh, vh, rows=rows[bh])["out"])
+    log(f"oracle dense reference on {sum(len(r) for r in rows)} rows: {time.perf_counter() - t0:.1f} s")
+    idx = [torch.from_numpy(r).to(q.device) for r in rows]
+    out = torch.empty_like(q)
+    ev = sol.HipEvents(4)
+    results = []
+    for beta in betas:
+        entry = {"beta": beta}
+        for mode, drop in (("pooled", False), ("dropped", True)):
+            _, dbg = sol.attn_fwd(q, k, v, beta, w.block, out=out, workspace=ws, debug=True,
+                                  drop_unselected=drop)
+            o32 = dbg["out_f32"].view(B * H, N, d)
+            num = den = 0.0
+            max_abs = 0.0
+            for bh in range(B * H):
+                g = o32[bh].index_select(0, idx[bh]).double().cpu().numpy()
+                diff = g - ref[bh]
+                num += float((diff ** 2).sum())
+                den += float((ref[bh] ** 2).sum())
+                max_abs = max(max_abs, float(np.abs(diff).max()))
+            ms = []
+            for i in range(steps + 2):
+                sol.attn_fwd(q, k, v, beta, w.block, out=out, workspace=ws, drop_unselected=drop,
+                             events=ev.handles)
+                torch.cuda.synchronize()
+                if i >= 2:
+                    ms.append(ev.elapsed_ms(2, 3))
+            entry[mode] = {"rel_l2_vs_dense": math.sqrt(num / den), "max_abs_vs_dense": max_abs,
+                           "fused_ms": sum(ms) / len(ms)}
+            if not drop:
+                M = sol.n_blocks(N, w.block)
+                tk = dbg["tile_kept"]
+                entry["rho_tile"] = float(tk.sum().item()) / (tk.numel() * M)
+                units = sol.union_units(dbg["mask"], N, w.block, heights=(1,))
+                entry["row_kept_key_fraction"] = units[1] / (B * H * N * N)
+            del dbg
+        log(f"beta {beta}: pooled rel-L2 {entry['pooled']['rel_l2_vs_dense']:.3e}, dropped "
+            f"{entry['dropped']['rel_l2_vs_dense']:.3e}, rho_tile {entry['rho_tile']:.4f}")
+        results.append(entry)
+    return {"ablation": "unselected blocks pooled (the method) vs dropped", "workload": w.name,
+            "rows_sampled": sum(len(r) for r in rows), "reference": "fp64 oracle dense attention",
+            "results": results}
+
+
 def recorded_traffic(kernel_sources, workload, beta):
     """HBM bytes per launch of the fused kernel, as recorded from rocprofv3 FETCH_SIZE/WRITE_SIZE
     counters (scaled by a plain-copy calibration) in profiles/sol_attn_wan_hbm_traffic.md, or
@@ -173,6 +233,9 @@ def main():
                     help="calibrate beta to this per-row kept density instead (the secondary "
                          "operating point)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ablation", default=None, metavar="BETAS",
+                    help="comma-separated betas: run the drop-vs-approximate ablation instead of the "
+                         "benchmark and print its JSON line")
     ap.add_argument("--cache", default=None, metavar="DIR",
                     help="keep the generated inputs in DIR (torch.save) and reuse them on later runs")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -228,6 +291,11 @@ def main():
     out = torch.empty_like(q)
     dout = torch.empty_like(q)
     ws = sol.new_workspace(q.shape, w.block)
+
+    if args.ablation:
+        betas = [float(x) for x in args.ablation.split(",")]
+        print(json.dumps(ablation(sol, w, q, k, v, ws, betas)), flush=True)
+        return
 
     if args.beta is not None:
         beta = args.beta
