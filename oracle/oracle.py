@@ -53,7 +53,9 @@ def load(path: str = _LIB):
     lib.sol_oracle_rows.argtypes = [p, p, p, i64, ci, ci, cd, p, i64, p, ci, p, p, p, p, p, p, p]
     lib.sol_oracle_select.argtypes = [p, p, i64, ci, ci, cd, p, p, p, p, p]
     lib.sol_oracle_dense_rows.argtypes = [p, p, p, i64, ci, p, i64, p, p]
-    for f in ("sol_oracle_pool", "sol_oracle_rows", "sol_oracle_select", "sol_oracle_dense_rows"):
+    lib.sol_oracle_route.argtypes = [p, p, i64, ci, ci, ci, cd, p, p, p]
+    for f in ("sol_oracle_pool", "sol_oracle_rows", "sol_oracle_select", "sol_oracle_dense_rows",
+              "sol_oracle_route"):
         getattr(lib, f).restype = ci
     lib.sol_oracle_threads.argtypes = []
     lib.sol_oracle_threads.restype = ci
@@ -163,6 +165,24 @@ def dense_rows(q, k, v, rows=None, lib=None) -> dict:
     if rc != 0:
         raise ValueError(f"sol_oracle_dense_rows failed ({rc})")
     return {"out": out, "lse": lse, "rows": rows}
+
+
+def route(q, k, block: int, mode: str, param: float, lib=None) -> dict:
+    """Prior-art routing on the same proxy for every row of one head: mode "topk" (param = k)
+    or "topp" (param = p); see sol_oracle_route.  Returns mask [N, W], gap [N], massgap [N]."""
+    lib = lib or load()
+    q, k = _f32(q), _f32(k)
+    N, d = q.shape
+    M = n_blocks(N, block)
+    W = (M + 31) // 32
+    res = {"mask": np.empty((N, W), np.uint32), "gap": np.empty(N, np.float64),
+           "massgap": np.empty(N, np.float64)}
+    m = {"topk": 0, "topp": 1}[mode]
+    rc = lib.sol_oracle_route(_ptr(q), _ptr(k), N, d, block, m, float(param), _ptr(res["mask"]),
+                              _ptr(res["gap"]), _ptr(res["massgap"]))
+    if rc != 0:
+        raise ValueError(f"sol_oracle_route failed ({rc})")
+    return res
 
 
 def mask_bits(mask: np.ndarray, M: int) -> np.ndarray:

@@ -303,5 +303,98 @@ int sol_oracle_dense_rows(const float* q, const float* k, const float* v, int64_
   return status;
 }
 
+/*
+ * Prior-art routing on the same proxy, for comparison ([routing] paragraph: top-k keeps a fixed
+ * number of blocks per query, top-p keeps blocks until their cumulative probability reaches a
+ * threshold; both need the whole proxy map first).  For every row of one head:
+ *   top-k (mode 0, param = k): keep the k blocks with the largest s_ij; among equal scores the
+ *     lower block index comes first.  k <= 0 keeps none, k >= M keeps all.
+ *   top-p (mode 1, param = p): the probability of block j is its share of the softmax over the
+ *     row's pooled logits, pi_j = exp(s_ij + ln n_j) / sum_l exp(s_il + ln n_l).  Blocks are taken
+ *     in decreasing order of pi (equal values: lower index first) and block j is kept when the
+ *     probability of the blocks before it is still below p.  p <= 0 keeps none, p >= 1 keeps all.
+ * Outputs: mask [N][W]; gap [N] (nullable): the score gap between the last kept block and the
+ * next one in the order (+inf if there is none), and, for top-p, massgap [N] (nullable): the
+ * smallest |cumulative probability before a block - p| over the row -- both measure how close the
+ * row's selection is to changing under rounding.
+ */
+typedef struct {
+  double key;
+  int64_t j;
+} route_item;
+
+static int route_cmp(const void* a, const void* b) {
+  const route_item* x = (const route_item*)a;
+  const route_item* y = (const route_item*)b;
+  if (x->key > y->key) return -1;
+  if (x->key < y->key) return 1;
+  return (x->j > y->j) - (x->j < y->j);
+}
+
+int sol_oracle_route(const float* q, const float* k, int64_t N, int d, int block, int mode,
+                     double param, uint32_t* mask, double* gap, double* massgap) {
+  if (!q || !k || !mask || N < 1 || d < 1 || block < 1 || (mode != 0 && mode != 1) || isnan(param))
+    return ORACLE_EINVAL;
+  const int64_t M = n_blocks(N, block);
+  const int64_t W = (M + 31) / 32;
+  const double inv_sqrt_d = 1.0 / sqrt((double)d);
+  double* kbar = (double*)malloc(sizeof(double) * (size_t)(M * d));
+  if (!kbar) return ORACLE_ENOMEM;
+  sol_oracle_pool(k, N, d, block, kbar);
+  int status = ORACLE_OK;
+#pragma omp parallel
+  {
+    route_item* it = (route_item*)malloc(sizeof(route_item) * (size_t)M);
+    double* w = (double*)malloc(sizeof(double) * (size_t)M);
+    if (!it || !w) {
+#pragma omp atomic write
+      status = ORACLE_ENOMEM;
+    } else {
+#pragma omp for schedule(static)
+      for (int64_t i = 0; i < N; ++i) {
+        const float* qi = q + i * d;
+        /* the proxy of every block; for top-p the ordering key is the pooled logit s + ln n */
+        for (int64_t j = 0; j < M; ++j) {
+          double sj = dot(qi, kbar + j * d, d) * inv_sqrt_d;
+          if (mode == 1) sj += log((double)(block_hi(j, N, block) - block_lo(j, block)));
+          it[j].key = sj;
+          it[j].j = j;
+        }
+        qsort(it, (size_t)M, sizeof(route_item), route_cmp);
+        for (int64_t x = 0; x < W; ++x) mask[i * W + x] = 0u;
+        int64_t kept = 0;
+        double mg = INFINITY;
+        if (mode == 0) {
+          kept = param <= 0.0 ? 0 : (param >= (double)M ? M : (int64_t)param);
+        } else if (param >= 1.0) {
+          kept = M;
+        } else if (param > 0.0) {
+          /* probabilities in the sorted order; the first key is the row maximum */
+          double z = 0.0;
+          for (int64_t r = 0; r < M; ++r) {
+            w[r] = exp(it[r].key - it[0].key);
+            z += w[r];
+          }
+          double before = 0.0;
+          for (int64_t r = 0; r < M; ++r) {
+            double frac = before / z;
+            double dist = fabs(frac - param);
+            if (dist < mg) mg = dist;
+            if (frac < param) kept = r + 1;
+            before += w[r];
+          }
+        }
+        for (int64_t r = 0; r < kept; ++r) mask[i * W + it[r].j / 32] |= 1u << (it[r].j % 32);
+        if (gap) gap[i] = (kept > 0 && kept < M) ? it[kept - 1].key - it[kept].key : INFINITY;
+        if (massgap) massgap[i] = mg;
+      }
+    }
+    free(it);
+    free(w);
+  }
+  free(kbar);
+  return status;
+}
+
 /* Threads the OpenMP loops above use (for reporting the CPU baseline's core count). */
 int sol_oracle_threads(void) { return omp_get_max_threads(); }

@@ -258,4 +258,70 @@ def pin_select_matches_rows(lib):
     assert np.abs(oracle.dense_rows(q, k, v, rows=[3, 7], lib=lib)["out"] - ref[[3, 7]]).max() < 1e-12
 
 
+def _route_brute(q, k, block, mode, param):
+    """Top-k / top-p selection written from the definition with numpy: proxies from the exact
+    logits (brute.proxy_scores), a stable sort, and a cumulative sum."""
+    s = brute.proxy_scores(q, k, block)
+    N, M = s.shape
+    n = np.array([b - a for a, b in brute.block_ranges(k.shape[0], block)], np.float64)
+    key = s + np.log(n)[None, :] if mode == "topp" else s
+    sel = np.zeros((N, M), bool)
+    for i in range(N):
+        order = sorted(range(M), key=lambda j: (-key[i, j], j))
+        if mode == "topk":
+            kk = 0 if param <= 0 else min(M, int(param))
+            sel[i, order[:kk]] = True
+        else:
+            if param >= 1:
+                sel[i] = True
+                continue
+            if param <= 0:
+                continue
+            w = np.exp(key[i] - key[i].max())
+            pr = w / w.sum()
+            before = 0.0
+            for j in order:
+                if before < param:
+                    sel[i, j] = True
+                before += pr[j]
+    return sel
+
+
+def pin_route_topk(lib):
+    """Top-k: brute force on random inputs (distinct scores), the limits k <= 0 and k >= M, and
+    ties broken toward the lower block index (q = 0 makes every score equal)."""
+    q, k, _ = _rand(11, N=70, d=8)
+    M = oracle.n_blocks(70, 8)
+    for kk in (1, 3, 5):
+        got = oracle.mask_bits(oracle.route(q, k, 8, "topk", kk, lib=lib)["mask"], M)
+        assert np.array_equal(got, _route_brute(q, k, 8, "topk", kk)), kk
+        assert (got.sum(axis=1) == kk).all()
+    assert not oracle.mask_bits(oracle.route(q, k, 8, "topk", 0, lib=lib)["mask"], M).any()
+    assert oracle.mask_bits(oracle.route(q, k, 8, "topk", M + 5, lib=lib)["mask"], M).all()
+    z = np.zeros_like(q)
+    got = oracle.mask_bits(oracle.route(z, k, 8, "topk", 4, lib=lib)["mask"], M)
+    assert (got[:, :4]).all() and not got[:, 4:].any()
+
+
+def pin_route_topp(lib):
+    """Top-p: brute force, the limits p <= 0 (none) and p >= 1 (all), a tiny p keeping only the
+    most probable block (pooled logit s + ln n, which favours the full blocks over the short last
+    one), and monotonicity in p."""
+    q, k, _ = _rand(12, N=70, d=8)
+    M = oracle.n_blocks(70, 8)
+    prev = None
+    for p in (0.05, 0.3, 0.6, 0.9):
+        got = oracle.mask_bits(oracle.route(q, k, 8, "topp", p, lib=lib)["mask"], M)
+        assert np.array_equal(got, _route_brute(q, k, 8, "topp", p)), p
+        if prev is not None:
+            assert (got | prev == got).all()
+        prev = got
+    assert not oracle.mask_bits(oracle.route(q, k, 8, "topp", 0.0, lib=lib)["mask"], M).any()
+    assert oracle.mask_bits(oracle.route(q, k, 8, "topp", 1.0, lib=lib)["mask"], M).all()
+    got = oracle.mask_bits(oracle.route(q, k, 8, "topp", 1e-12, lib=lib)["mask"], M)
+    s = brute.proxy_scores(q, k, 8) + np.log([min(8, 70 - 8 * j) for j in range(M)])[None, :]
+    assert (got.sum(axis=1) == 1).all()
+    assert (np.argmax(got, axis=1) == np.argmax(s, axis=1)).all()
+
+
 PINS = [f for n, f in sorted(globals().items()) if n.startswith("pin_") and callable(f)]

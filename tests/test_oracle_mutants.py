@@ -31,6 +31,10 @@ MUTANTS = {
     "mean_off_by_one": ("m1 /= (double)M;\n        double m2 = 0.0;\n        for (int64_t j = 0; j < M; ++j) m2 += (s[j] - m1) * (s[j] - m1);\n        double sd = sqrt(m2 / (double)M);\n\n",
                         "m1 /= (double)(M + 1);\n        double m2 = 0.0;\n        for (int64_t j = 0; j < M; ++j) m2 += (s[j] - m1) * (s[j] - m1);\n        double sd = sqrt(m2 / (double)M);\n\n"),
     "last_block_short": ("return hi < N ? hi : N;", "return hi < N ? hi : N - 1;"),
+    "route_ties_high_index_first": ("return (x->j > y->j) - (x->j < y->j);",
+                                    "return (x->j < y->j) - (x->j > y->j);"),
+    "topp_without_block_size": ("if (mode == 1) sj += log(", "if (mode == 2) sj += log("),
+    "topp_counts_blocks_not_mass": ("w[r] = exp(it[r].key - it[0].key);", "w[r] = 1.0;"),
 }
 
 
