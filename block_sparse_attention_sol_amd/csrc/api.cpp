@@ -148,15 +148,20 @@ int sol_pool_kv(const sol_shape* shape, const void* k, const void* v, int block,
                     "pool kernel launch");
 }
 
-int sol_attn_fwd_ex(const sol_shape* shape, const void* q, const void* k, const void* v,
-                    float beta, int block, void* out, void* workspace, size_t workspace_bytes,
-                    const sol_attn_debug* dbg, void* stream) {
+namespace {
+
+// sol_attn_fwd_ex and sol_attn_fwd_masked: with mask_in the caller's selection replaces the
+// threshold (no row statistics are computed) and `drop` comes from the argument.
+int attn_forward(const sol_shape* shape, const void* q, const void* k, const void* v, float beta,
+                 int block, void* out, void* workspace, size_t workspace_bytes,
+                 const sol_attn_debug* dbg, const uint32_t* mask_in, int drop_in, void* stream) {
   int st;
   if ((st = check_shape(shape)) || (st = check_block(block))) return st;
   if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
       (st = check_tensor(out, "out")))
     return st;
-  if (std::isnan(beta)) return fail(SOL_EINVAL, "beta is NaN");
+  if (!mask_in && std::isnan(beta)) return fail(SOL_EINVAL, "beta is NaN");
+  if (mask_in && ((uintptr_t)mask_in & 3u)) return fail(SOL_EINVAL, "mask is not 4-byte aligned");
   const Workspace w = layout(*shape, block);
   if (!workspace) return fail(SOL_EWORKSPACE, "workspace is NULL (need %zu bytes)", w.total);
   if (!aligned16(workspace)) return fail(SOL_EINVAL, "workspace is not 16-byte aligned");
@@ -199,23 +204,25 @@ int sol_attn_fwd_ex(const sol_shape* shape, const void* q, const void* k, const 
   e = solattn::launch_pool(d, BH, shape->N, block, k, v, kbar, nullptr, kp, vbt, Mp, s);
   if (e != hipSuccess) return hip_status(e, "pool kernel launch");
   if ((e = mark(1)) != hipSuccess) return hip_status(e, "event record");
-  e = solattn::launch_kstats(d, BH, M, kbar, kglob, kglob64, cp, s);
-  if (e != hipSuccess) return hip_status(e, "pooled-key statistics launch");
-  solattn::RowStatsArgs r{};
-  r.q = (const uint16_t*)q;
-  r.cp = cp;
-  r.kglob = kglob;
-  r.BH = BH;
-  r.N = shape->N;
-  r.beta = beta;
-  r.tau = tau;
-  if (dbg) {
-    r.mu = dbg->mu;
-    r.sigma = dbg->sigma;
-    r.tau_out = dbg->tau;
+  if (!mask_in) {
+    e = solattn::launch_kstats(d, BH, M, kbar, kglob, kglob64, cp, s);
+    if (e != hipSuccess) return hip_status(e, "pooled-key statistics launch");
+    solattn::RowStatsArgs r{};
+    r.q = (const uint16_t*)q;
+    r.cp = cp;
+    r.kglob = kglob;
+    r.BH = BH;
+    r.N = shape->N;
+    r.beta = beta;
+    r.tau = tau;
+    if (dbg) {
+      r.mu = dbg->mu;
+      r.sigma = dbg->sigma;
+      r.tau_out = dbg->tau;
+    }
+    e = solattn::launch_rowstats(d, r, s);
+    if (e != hipSuccess) return hip_status(e, "row statistics launch");
   }
-  e = solattn::launch_rowstats(d, r, s);
-  if (e != hipSuccess) return hip_status(e, "row statistics launch");
   if ((e = mark(2)) != hipSuccess) return hip_status(e, "event record");
 
   solattn::SparseArgs a{};
@@ -227,14 +234,16 @@ int sol_attn_fwd_ex(const sol_shape* shape, const void* q, const void* k, const 
   a.vbt = vbt;
   a.tau = tau;
   a.rowmask = rowmask;
+  a.mask_in = mask_in;
   a.mask_out = dbg ? dbg->mask : nullptr;
   a.BH = BH;
   a.N = shape->N;
   a.M = M;
   a.Mp = Mp;
   a.block = block;
+  a.drop = drop_in;
   if (dbg) {
-    a.drop = dbg->drop_unselected ? 1 : 0;
+    if (!mask_in) a.drop = dbg->drop_unselected ? 1 : 0;
     a.lse = dbg->lse;
     a.tile_kept = dbg->tile_kept;
     a.out_f32 = dbg->out_f32;
@@ -242,6 +251,81 @@ int sol_attn_fwd_ex(const sol_shape* shape, const void* q, const void* k, const 
   e = solattn::launch_sparse(d, a, s);
   if (e != hipSuccess) return hip_status(e, "sparse attention kernel launch");
   return hip_status(mark(3), "event record");
+}
+
+}  // namespace
+
+int sol_attn_fwd_ex(const sol_shape* shape, const void* q, const void* k, const void* v,
+                    float beta, int block, void* out, void* workspace, size_t workspace_bytes,
+                    const sol_attn_debug* dbg, void* stream) {
+  return attn_forward(shape, q, k, v, beta, block, out, workspace, workspace_bytes, dbg, nullptr, 0,
+                      stream);
+}
+
+int sol_attn_fwd_masked(const sol_shape* shape, const void* q, const void* k, const void* v,
+                        const uint32_t* mask, int block, int drop_unselected, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!mask) return fail(SOL_EINVAL, "mask is NULL");
+  return attn_forward(shape, q, k, v, 0.f, block, out, workspace, workspace_bytes, nullptr, mask,
+                      drop_unselected ? 1 : 0, stream);
+}
+
+int sol_proxy_map(const sol_shape* shape, const void* q, const void* k, int block, float* s_map,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  int st;
+  if ((st = check_shape(shape)) || (st = check_block(block))) return st;
+  if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) ||
+      (st = check_tensor(s_map, "s_map")))
+    return st;
+  const Workspace w = layout(*shape, block);
+  if (!workspace) return fail(SOL_EWORKSPACE, "workspace is NULL (need %zu bytes)", w.total);
+  if (!aligned16(workspace)) return fail(SOL_EINVAL, "workspace is not 16-byte aligned");
+  if (workspace_bytes < w.total)
+    return fail(SOL_EWORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, w.total);
+  const int64_t BH = shape->B * shape->H;
+  const int64_t M = n_blocks(shape->N, block);
+  const int64_t Mp = padded_blocks(shape->N, block);
+  if (overlaps(s_map, (size_t)(BH * M * shape->N) * sizeof(float), workspace, w.total))
+    return fail(SOL_EINVAL, "s_map overlaps the workspace");
+  unsigned char* ws = (unsigned char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = solattn::launch_pool((int)shape->d, BH, shape->N, block, k, k, (float*)(ws + w.kbar),
+                                      nullptr, (uint16_t*)(ws + w.kp), (uint16_t*)(ws + w.vbt), Mp, s);
+  if (e != hipSuccess) return hip_status(e, "pool kernel launch");
+  return hip_status(solattn::launch_proxy_map((int)shape->d, (const uint16_t*)q,
+                                              (const uint16_t*)(ws + w.kp), BH, shape->N, M, Mp,
+                                              s_map, s),
+                    "proxy map kernel launch");
+}
+
+namespace {
+int route_select(const sol_shape* shape, int block, const float* s_map, int mode, int64_t k, float p,
+                 uint32_t* mask, void* stream) {
+  int st;
+  if ((st = check_shape(shape)) || (st = check_block(block))) return st;
+  if ((st = check_tensor(s_map, "s_map"))) return st;
+  if (!mask) return fail(SOL_EINVAL, "mask is NULL");
+  if ((uintptr_t)mask & 3u) return fail(SOL_EINVAL, "mask is not 4-byte aligned");
+  if (mode == 1 && std::isnan(p)) return fail(SOL_EINVAL, "p is NaN");
+  const int64_t BH = shape->B * shape->H;
+  const int64_t M = n_blocks(shape->N, block);
+  const int64_t W = (M + 31) / 32;
+  if (overlaps(mask, (size_t)(BH * shape->N * W) * 4, s_map, (size_t)(BH * M * shape->N) * 4))
+    return fail(SOL_EINVAL, "mask overlaps s_map");
+  return hip_status(solattn::launch_route_select(mode, s_map, BH, shape->N, M, block, k, p, mask,
+                                                 (hipStream_t)stream),
+                    "selection kernel launch");
+}
+}  // namespace
+
+int sol_select_topk(const sol_shape* shape, int block, const float* s_map, int64_t k,
+                    uint32_t* mask, void* stream) {
+  return route_select(shape, block, s_map, 0, k, 0.f, mask, stream);
+}
+
+int sol_select_topp(const sol_shape* shape, int block, const float* s_map, float p, uint32_t* mask,
+                    void* stream) {
+  return route_select(shape, block, s_map, 1, 0, p, mask, stream);
 }
 
 int sol_attn_fwd(const sol_shape* shape, const void* q, const void* k, const void* v, float beta,

@@ -674,7 +674,8 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
 
   bf16x8 qf[D / 16];
   load_q<D>(qb + row * D, rvalid, qf);
-  const float tau = rvalid ? a.tau[bh * a.N + row] : INFINITY;  // padding rows keep nothing
+  // padding rows keep nothing; with a caller's selection the threshold is not used
+  const float tau = (rvalid && !a.mask_in) ? a.tau[bh * a.N + row] : INFINITY;
   // s >= tau  <=>  raw dot product >= tau * sqrt(d)  (compared in fp32)
   const float tau_raw = tau * sqrtf((float)D);
 
@@ -705,12 +706,20 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
     load_tile<D, 32>(kp0, (int64_t)cb * 32, a.Mp, base + 2 * kChunkTile);
     load_vbt_chunk<D>(vt0, a.Mp, cb, base + 3 * kChunkTile);
   };
+  // the caller's selection word of this row for chunk cb (loaded one chunk ahead, with the copy)
+  const uint32_t* min_row = a.mask_in ? a.mask_in + (bh * a.N + row) * W : nullptr;
+  auto in_word = [&](int cb) -> uint32_t { return (min_row && rvalid) ? min_row[cb] : 0u; };
   issue_chunk(0, 0);
+  uint32_t win_next = in_word(0);
   for (int cb = 0; cb < nchunks; ++cb) {
     const int b = cb & 1;
     wait_vmcnt<0>();
     bar();  // publishes chunk cb, retires chunk cb - 1's buffer
-    if (cb + 1 < nchunks) issue_chunk(cb + 1, b ^ 1);
+    const uint32_t win = win_next;
+    if (cb + 1 < nchunks) {
+      issue_chunk(cb + 1, b ^ 1);
+      win_next = in_word(cb + 1);
+    }
     const lds_u8* base = smem + b * kRouteBuf;
     f32x16 acc = {};
 #pragma unroll
@@ -723,7 +732,7 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int kj = key_of(v, h);
-        const bool sel = acc[v] >= tau_raw;
+        const bool sel = min_row ? ((win >> kj) & 1u) != 0u : acc[v] >= tau_raw;
         bits |= (sel ? 1u : 0u) << kj;
         x[v] = sel ? -INFINITY : fmaf(acc[v], sl2, l2n_full);
         cmax = fmaxf(cmax, x[v]);
@@ -733,7 +742,7 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
       for (int v = 0; v < 16; ++v) {
         const int kj = key_of(v, h);
         const bool valid = kj < nvalid;
-        const bool sel = valid && acc[v] >= tau_raw;
+        const bool sel = valid && (min_row ? ((win >> kj) & 1u) != 0u : acc[v] >= tau_raw);
         bits |= (sel ? 1u : 0u) << kj;
         x[v] = (valid && !sel) ? fmaf(acc[v], sl2, kj == nvalid - 1 ? l2n_last : l2n_full)
                                : -INFINITY;
@@ -910,6 +919,64 @@ __device__ __forceinline__ void dense_half(int n, int nst, int64_t N, const uint
 }
 
 // ---------------------------------------------------------------------------------------------
+// Full proxy map (the prior-art routing's input): s_map[bh][j][i] = q_i . Kbar_j / sqrt(d) for
+// every row and block, written to memory -- the round trip the fused kernel avoids.  The same
+// fp32-accurate three-piece product as the fused kernel's routing sweep, one workgroup per
+// 128-row tile, pooled-key chunks double buffered; block-major so that a wave's 32 rows store one
+// contiguous run per block.
+// ---------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void proxy_map_kernel(const uint16_t* __restrict__ q,
+                                                                const uint16_t* __restrict__ kp,
+                                                                int64_t BH, int64_t N, int64_t M,
+                                                                int64_t Mp, float* __restrict__ smap) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  lds_u8* smem = (lds_u8*)smem_raw;
+  constexpr int kChunkTile = 32 * D * 2;
+  constexpr int kBuf = 3 * kChunkTile;
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63, c = lane & 31, h = lane >> 5;
+  const int64_t ntiles = (N + kQTile - 1) / kQTile;
+  int64_t w;
+  if (!work_item(BH * ntiles, w)) return;
+  const int64_t bh = w / ntiles;
+  const int64_t tile = w % ntiles;
+  const int64_t row = tile * kQTile + wave * 32 + c;
+  const bool rvalid = row < N;
+  bf16x8 qf[D / 16];
+  load_q<D>(q + (bh * N + row) * D, rvalid, qf);
+  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+  const int64_t piece = BH * Mp * D;
+  const uint16_t* kp0 = kp + bh * Mp * D;
+  float* out = smap + bh * M * N + row;
+  const int nchunks = (int)(Mp / 32);
+  auto issue_chunk = [&](int cb, int b) {
+    lds_u8* base = smem + b * kBuf;
+    load_tile<D, 32>(kp0 + 2 * piece, (int64_t)cb * 32, Mp, base);
+    load_tile<D, 32>(kp0 + 1 * piece, (int64_t)cb * 32, Mp, base + kChunkTile);
+    load_tile<D, 32>(kp0, (int64_t)cb * 32, Mp, base + 2 * kChunkTile);
+  };
+  issue_chunk(0, 0);
+  for (int cb = 0; cb < nchunks; ++cb) {
+    const int b = cb & 1;
+    wait_vmcnt<0>();
+    bar();
+    if (cb + 1 < nchunks) issue_chunk(cb + 1, b ^ 1);
+    const lds_u8* base = smem + b * kBuf;
+    f32x16 acc = {};
+#pragma unroll
+    for (int p = 0; p < 3; ++p) acc = scores32<D>(base + p * kChunkTile, 0, qf, acc);
+    if (rvalid) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t j = (int64_t)cb * 32 + key_of(v, h);
+        if (j < M) out[j * N] = acc[v] * inv_sqrt_d;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Dense reference kernel: the exact loop over every key, no routing.
 // ---------------------------------------------------------------------------------------------
 
@@ -1038,6 +1105,25 @@ static hipError_t launch_rowstats_t(const RowStatsArgs& a, hipStream_t stream) {
   const int64_t groups = (ntiles + kRowStatsTiles - 1) / kRowStatsTiles;
   hipLaunchKernelGGL(kern, dim3((unsigned)(a.BH * groups)), dim3(kThreads), smem, stream, a);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_proxy_map_t(const uint16_t* q, const uint16_t* kp, int64_t BH, int64_t N,
+                                     int64_t M, int64_t Mp, float* s_map, hipStream_t stream) {
+  const size_t smem = (size_t)2 * 3 * 32 * D * 2;
+  auto kern = proxy_map_kernel<D>;
+  hipError_t err = set_smem(kern, smem);
+  if (err != hipSuccess) return err;
+  const int64_t ntiles = (N + kQTile - 1) / kQTile;
+  hipLaunchKernelGGL(kern, dim3(xcd_grid(BH * ntiles)), dim3(kThreads), smem, stream, q, kp, BH, N,
+                     M, Mp, s_map);
+  return hipGetLastError();
+}
+
+hipError_t launch_proxy_map(int d, const uint16_t* q, const uint16_t* kp, int64_t BH, int64_t N,
+                            int64_t M, int64_t Mp, float* s_map, hipStream_t stream) {
+  return d == 64 ? launch_proxy_map_t<64>(q, kp, BH, N, M, Mp, s_map, stream)
+                 : launch_proxy_map_t<128>(q, kp, BH, N, M, Mp, s_map, stream);
 }
 
 hipError_t launch_rowstats(int d, const RowStatsArgs& a, hipStream_t stream) {

@@ -41,6 +41,7 @@ struct SparseArgs {
   int64_t BH, N, M, Mp;
   int block;
   int drop;
+  const uint32_t* mask_in;  // [BH][N][Mp/32] caller's selection (replaces s >= tau), or NULL
   // optional outputs
   uint32_t* mask_out;   // [BH][N][Mp/32] selection words, row-major
   float* lse;
@@ -51,6 +52,15 @@ hipError_t launch_sparse(int d, const SparseArgs& a, hipStream_t stream);
 
 hipError_t launch_dense(int d, int64_t BH, int64_t N, const void* q, const void* k, const void* v,
                         void* out, float* lse, hipStream_t stream);
+
+// Full proxy map s_map[BH][M][N] = q . Kbar_j / sqrt(d) (fp32, block-major) from the pooled-key
+// pieces kp [3][BH][Mp][d].
+hipError_t launch_proxy_map(int d, const uint16_t* q, const uint16_t* kp, int64_t BH, int64_t N,
+                            int64_t M, int64_t Mp, float* s_map, hipStream_t stream);
+// Top-k (mode 0, count k) or top-p (mode 1, probability p) selection per row from s_map, written as
+// mask [BH][N][ceil(M/32)].
+hipError_t launch_route_select(int mode, const float* s_map, int64_t BH, int64_t N, int64_t M,
+                               int block, int64_t k, float p, uint32_t* mask, hipStream_t stream);
 
 // Matrix-core rate probe: `workgroups` x 4 waves, each issuing iters x mfma_probe_chains()
 // independent bf16 32x32x16 MFMAs.

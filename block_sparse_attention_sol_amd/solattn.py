@@ -26,6 +26,10 @@ EXPORTS = (
     "sol_pool_kv",
     "sol_attn_fwd",
     "sol_attn_fwd_ex",
+    "sol_attn_fwd_masked",
+    "sol_proxy_map",
+    "sol_select_topk",
+    "sol_select_topp",
     "sol_mfma_probe",
     "sol_dense_fwd",
     "sol_status_str",
@@ -76,7 +80,12 @@ def load_library(path: str = LIB_PATH):
                                     ctypes.POINTER(SolAttnDebug), vp]
     lib.sol_dense_fwd.argtypes = [shp, vp, vp, vp, vp, vp, vp]
     lib.sol_mfma_probe.argtypes = [ci, ci, vp, vp]
-    for f in ("sol_pool_kv", "sol_attn_fwd", "sol_attn_fwd_ex", "sol_dense_fwd", "sol_mfma_probe"):
+    lib.sol_attn_fwd_masked.argtypes = [shp, vp, vp, vp, vp, ci, ci, vp, vp, sz, vp]
+    lib.sol_proxy_map.argtypes = [shp, vp, vp, ci, vp, vp, sz, vp]
+    lib.sol_select_topk.argtypes = [shp, ci, vp, ctypes.c_int64, vp, vp]
+    lib.sol_select_topp.argtypes = [shp, ci, vp, cf, vp, vp]
+    for f in ("sol_pool_kv", "sol_attn_fwd", "sol_attn_fwd_ex", "sol_dense_fwd", "sol_mfma_probe",
+              "sol_attn_fwd_masked", "sol_proxy_map", "sol_select_topk", "sol_select_topp"):
         getattr(lib, f).restype = ci
     lib.sol_status_str.argtypes = [ci]
     lib.sol_status_str.restype = ctypes.c_char_p
@@ -207,6 +216,65 @@ def dense_fwd(q, k, v, out=None, want_lse: bool = False, stream=None):
                              _dev(out, "out"), _dev(lse, "lse") if lse is not None else None,
                              _stream(stream)))
     return (out, lse) if want_lse else out
+
+
+def proxy_map(q, k, block: int, s_map=None, workspace=None, stream=None):
+    """Full proxy map s_map [B, H, M, N] fp32 (block-major) of the prior-art routing pipeline."""
+    import torch
+    lib = load_library()
+    B, H, N, d = q.shape
+    M = n_blocks(N, block)
+    if s_map is None:
+        s_map = torch.empty((B, H, M, N), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(q.shape, block, q.device)
+    _check(lib.sol_proxy_map(ctypes.byref(_shape(q)), _dev(q, "q"), _dev(k, "k"), block,
+                             _dev(s_map, "s_map"), _dev(workspace, "workspace"), workspace.numel(),
+                             _stream(stream)))
+    return s_map
+
+
+def _route_mask(q_shape, block, device):
+    import torch
+    B, H, N, _ = q_shape
+    W = (n_blocks(N, block) + 31) // 32
+    return torch.empty((B, H, N, W), dtype=torch.int32, device=device)
+
+
+def select_topk(s_map, q_shape, block: int, k: int, mask=None, stream=None):
+    """Top-k block selection per row from s_map; returns mask [B, H, N, ceil(M/32)] int32."""
+    lib = load_library()
+    if mask is None:
+        mask = _route_mask(q_shape, block, s_map.device)
+    _check(lib.sol_select_topk(ctypes.byref(SolShape(*q_shape)), block, _dev(s_map, "s_map"),
+                               int(k), _dev(mask, "mask"), _stream(stream)))
+    return mask
+
+
+def select_topp(s_map, q_shape, block: int, p: float, mask=None, stream=None):
+    """Top-p block selection per row from s_map; returns mask [B, H, N, ceil(M/32)] int32."""
+    lib = load_library()
+    if mask is None:
+        mask = _route_mask(q_shape, block, s_map.device)
+    _check(lib.sol_select_topp(ctypes.byref(SolShape(*q_shape)), block, _dev(s_map, "s_map"),
+                               float(p), _dev(mask, "mask"), _stream(stream)))
+    return mask
+
+
+def attn_fwd_masked(q, k, v, mask, block: int, drop_unselected: bool = False, out=None,
+                    workspace=None, stream=None):
+    """Sol-Attn forward with the caller's selection mask [B, H, N, ceil(M/32)] (int32 words)."""
+    import torch
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = new_workspace(q.shape, block, q.device)
+    _check(lib.sol_attn_fwd_masked(ctypes.byref(_shape(q)), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+                                   _dev(mask, "mask"), block, int(bool(drop_unselected)),
+                                   _dev(out, "out"), _dev(workspace, "workspace"), workspace.numel(),
+                                   _stream(stream)))
+    return out
 
 
 MFMA_PROBE_FLOPS_PER_WAVE_ITER = 8 * 32768  # 8 independent 32x32x16 bf16 MFMAs

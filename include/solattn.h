@@ -120,6 +120,52 @@ int sol_dense_fwd(const sol_shape* shape, const void* q, const void* k, const vo
                   float* lse, void* stream);
 
 /*
+ * Prior-art routing, for comparison (page above, paragraph on routing: top-k keeps a fixed number
+ * of key blocks per query, top-p keeps blocks until their cumulative probability reaches a
+ * threshold, and both need the full proxy map in memory before the sparse pass).  These calls
+ * build that pipeline from the same proxy as sol_attn_fwd: map -> selection -> attention with the
+ * caller's selection.
+ *
+ * sol_proxy_map: s_map[b][h][j][i] = q_i . Kbar_j / sqrt(d) for every query row i and key block j
+ * (fp32, block-major: [B][H][M][N], B*H*M*N*4 bytes, device, written; the same fp32-accurate
+ * values the fused kernel compares with tau).  Pools K into the workspace first (the workspace
+ * of sol_attn_workspace_bytes(shape, block), contents scratch).  s_map must not overlap the
+ * workspace.
+ */
+int sol_proxy_map(const sol_shape* shape, const void* q, const void* k, int block, float* s_map,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Top-k selection from s_map: for each row, the k blocks with the largest s_ij, equal scores
+ * keeping the lower block index first.  k <= 0 keeps none, k >= M keeps all.
+ *   mask  [B][H][N][ceil(M/32)] uint32, device, written (bit j%32 of word j/32 = block j kept).
+ */
+int sol_select_topk(const sol_shape* shape, int block, const float* s_map, int64_t k,
+                    uint32_t* mask, void* stream);
+
+/*
+ * Top-p selection from s_map: the probability of block j in row i is its share of the softmax
+ * over the row's pooled logits s_ij + ln n_j; blocks are taken in decreasing order of probability
+ * (equal values: lower index first) and a block is kept while the probability of the blocks before
+ * it is below p.  p <= 0 keeps none, p >= 1 keeps all, NaN -> SOL_EINVAL.  Sums in fp32: a row
+ * whose cumulative probability passes within rounding of p at a block may decide that block
+ * either way.  mask as for sol_select_topk.
+ */
+int sol_select_topp(const sol_shape* shape, int block, const float* s_map, float p,
+                    uint32_t* mask, void* stream);
+
+/*
+ * sol_attn_fwd with the caller's selection instead of the threshold: block j is computed exactly
+ * for row i iff bit j of mask[b][h][i] is set ([B][H][N][ceil(M/32)] uint32, device, read; bits
+ * at or beyond M are ignored).  Unselected blocks enter as pooled tokens, or are dropped when
+ * drop_unselected is non-zero (a row with nothing kept then outputs 0).  No row statistics are
+ * computed.  Other arguments and errors as for sol_attn_fwd.
+ */
+int sol_attn_fwd_masked(const sol_shape* shape, const void* q, const void* k, const void* v,
+                        const uint32_t* mask, int block, int drop_unselected, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Matrix-core rate probe (measurement only, not part of the attention path): `workgroups`
  * workgroups of 4 waves each issue iters x 8 independent bf16 32x32x16 MFMAs (32768 FLOPs each)
  * on register operands, so FLOPs = workgroups * 4 * iters * 8 * 32768.  sink (device,

@@ -165,3 +165,26 @@ def test_mfma_probe_rejects(lib):
     assert lib.sol_mfma_probe(8, 0, sink, None) == solattn.SOL_EINVAL
     assert lib.sol_mfma_probe(8, 10, None, None) == solattn.SOL_EINVAL
     assert b"sink" in lib.sol_last_error()
+
+
+def test_routing_entries_reject(lib):
+    s = _shape()
+    q, k, v, out, ws, smap, mask = _ptrs(7)
+    need = lib.sol_attn_workspace_bytes(ctypes.byref(s), 128)
+    nan = float("nan")
+    assert lib.sol_attn_fwd_masked(ctypes.byref(s), q, k, v, None, 128, 0, out, ws, need,
+                                   None) == solattn.SOL_EINVAL
+    assert b"mask" in lib.sol_last_error()
+    assert lib.sol_attn_fwd_masked(ctypes.byref(s), q, k, v, FAKE + 2, 128, 0, out, ws, need,
+                                   None) == solattn.SOL_EINVAL
+    assert lib.sol_attn_fwd_masked(ctypes.byref(s), q, k, v, mask, 128, 0, out, ws, 16,
+                                   None) == solattn.SOL_EWORKSPACE
+    assert lib.sol_proxy_map(ctypes.byref(s), q, k, 100, smap, ws, need, None) == solattn.SOL_EUNSUPPORTED
+    assert lib.sol_proxy_map(ctypes.byref(s), q, k, 128, smap, ws, 16, None) == solattn.SOL_EWORKSPACE
+    assert lib.sol_proxy_map(ctypes.byref(s), q, None, 128, smap, ws, need, None) == solattn.SOL_EINVAL
+    assert lib.sol_proxy_map(ctypes.byref(s), q, k, 128, ws, ws, need, None) == solattn.SOL_EINVAL
+    assert lib.sol_select_topk(ctypes.byref(s), 128, smap, 3, None, None) == solattn.SOL_EINVAL
+    assert lib.sol_select_topk(ctypes.byref(s), 96, smap, 3, mask, None) == solattn.SOL_EUNSUPPORTED
+    assert lib.sol_select_topp(ctypes.byref(s), 128, smap, nan, mask, None) == solattn.SOL_EINVAL
+    assert lib.sol_select_topp(ctypes.byref(s), 128, None, 0.5, mask, None) == solattn.SOL_EINVAL
+    assert lib.sol_select_topp(ctypes.byref(s), 128, smap, 0.5, smap, None) == solattn.SOL_EINVAL
