@@ -197,6 +197,73 @@ def ablation(sol, w, q, k, v, ws, betas, rows_per_head=48, steps=5):
             "results": results}
 
 
+def routing_comparison(sol, w, q, k, v, ws, spec, steps=5, warmup=2):
+    """The prior-art pipeline the fused pass replaces: full proxy map in memory, top-k or top-p
+    selection from it, then attention with that selection (pooled unselected blocks, as in the
+    method, so that only the routing differs).  Each stage is timed with events; the fused
+    Sol-Attn forward is timed at the beta whose kept-block density (128-row tiles) matches."""
+    import torch
+    mode, prm = spec.split(":")
+    prm = int(prm) if mode == "topk" else float(prm)
+    B, H, N, d = q.shape
+    M = sol.n_blocks(N, w.block)
+    smap = torch.empty((B, H, N, M), dtype=torch.float32, device=q.device)
+    sel = torch.empty((B, H, N, (M + 31) // 32), dtype=torch.int32, device=q.device)
+    out = torch.empty_like(q)
+
+    def timed(fn):
+        ts = []
+        for i in range(warmup + steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= warmup:
+                ts.append(e0.elapsed_time(e1))
+        return sum(ts) / len(ts)
+
+    t_map = timed(lambda: sol.proxy_map(q, k, w.block, s_map=smap, workspace=ws))
+    if mode == "topk":
+        t_sel = timed(lambda: sol.select_topk(smap, tuple(q.shape), w.block, prm, mask=sel))
+    else:
+        t_sel = timed(lambda: sol.select_topp(smap, tuple(q.shape), w.block, prm, mask=sel))
+    t_attn = timed(lambda: sol.attn_fwd_masked(q, k, v, sel, w.block, out=out, workspace=ws))
+    units = sol.union_units(sel, N, w.block, heights=(1, 128))
+    F_tile = 4.0 * d * units[128]
+    # union density at 128-row tiles, counted in blocks
+    shifts = torch.arange(32, device=q.device, dtype=torch.int32)
+    kept_tiles = 0
+    T = (N + 127) // 128
+    for b in range(B):
+        for h in range(H):
+            bits = ((sel[b, h].unsqueeze(-1) >> shifts) & 1).to(torch.uint8).reshape(N, -1)[:, :M]
+            bits = torch.nn.functional.pad(bits, (0, 0, 0, T * 128 - N))
+            kept_tiles += int(bits.view(T, 128, M).amax(dim=1).sum().item())
+    rho_tile = kept_tiles / (B * H * T * M)
+    log(f"{spec}: map {t_map:.2f} ms, select {t_sel:.2f} ms, attention {t_attn:.2f} ms, "
+        f"rho_tile {rho_tile:.4f}")
+    beta = calibrate_beta(sol, q, k, v, w.block, rho_tile, ws, out)
+    t_sol = timed(lambda: sol.attn_fwd(q, k, v, beta, w.block, out=out, workspace=ws))
+    t_dense = timed(lambda: sol.dense_fwd(q, k, v, out=out), ) if N <= 131072 else None
+    map_bytes = 4.0 * B * H * M * N
+    passes = 1  # the selection reads the map once
+    return {
+        "routing_comparison": spec, "workload": w.name,
+        "prior_art_ms": {"proxy_map": t_map, "select": t_sel, "attention": t_attn,
+                         "total": t_map + t_sel + t_attn},
+        "prior_art_rho_tile": rho_tile,
+        "prior_art_rho_row_keys": units[1] / (B * H * N * N),
+        "prior_art_tflops_on_tile_flops": F_tile / ((t_map + t_sel + t_attn) * 1e-3) / 1e12,
+        "proxy_map_bytes": map_bytes,
+        "proxy_map_round_trip_bytes": map_bytes * (1 + passes),
+        "sol_attn_beta_at_same_rho_tile": beta,
+        "sol_attn_ms": t_sol,
+        "sol_attn_speedup_over_prior_art": (t_map + t_sel + t_attn) / t_sol,
+        "dense_ms": t_dense,
+    }
+
+
 def recorded_traffic(kernel_sources, workload, beta):
     """HBM bytes per launch of the fused kernel, as recorded from rocprofv3 FETCH_SIZE/WRITE_SIZE
     counters (scaled by a plain-copy calibration) in profiles/sol_attn_wan_hbm_traffic.md, or
@@ -236,6 +303,10 @@ def main():
     ap.add_argument("--ablation", default=None, metavar="BETAS",
                     help="comma-separated betas: run the drop-vs-approximate ablation instead of the "
                          "benchmark and print its JSON line")
+    ap.add_argument("--routing", default=None, metavar="topk:K|topp:P",
+                    help="time the prior-art pipeline (materialised proxy map, top-k/top-p "
+                         "selection, attention) against the fused pass at matched density and "
+                         "print its JSON line instead of the benchmark")
     ap.add_argument("--cache", default=None, metavar="DIR",
                     help="keep the generated inputs in DIR (torch.save) and reuse them on later runs")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -291,6 +362,10 @@ def main():
     out = torch.empty_like(q)
     dout = torch.empty_like(q)
     ws = sol.new_workspace(q.shape, w.block)
+
+    if args.routing:
+        print(json.dumps(routing_comparison(sol, w, q, k, v, ws, args.routing)), flush=True)
+        return
 
     if args.ablation:
         betas = [float(x) for x in args.ablation.split(",")]

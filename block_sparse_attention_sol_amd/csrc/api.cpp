@@ -310,6 +310,11 @@ int route_select(const sol_shape* shape, int block, const float* s_map, int mode
   const int64_t BH = shape->B * shape->H;
   const int64_t M = n_blocks(shape->N, block);
   const int64_t W = (M + 31) / 32;
+  if (M > solattn::route_max_blocks())
+    return fail(SOL_EUNSUPPORTED, "selection supports at most %lld key blocks per row (got %lld)",
+                (long long)solattn::route_max_blocks(), (long long)M);
+  if (BH * shape->N > (int64_t)4 * 0x7fffffff)
+    return fail(SOL_EUNSUPPORTED, "selection supports at most %lld rows in all", 4LL * 0x7fffffff);
   if (overlaps(mask, (size_t)(BH * shape->N * W) * 4, s_map, (size_t)(BH * M * shape->N) * 4))
     return fail(SOL_EINVAL, "mask overlaps s_map");
   return hip_status(solattn::launch_route_select(mode, s_map, BH, shape->N, M, block, k, p, mask,

@@ -919,11 +919,11 @@ __device__ __forceinline__ void dense_half(int n, int nst, int64_t N, const uint
 }
 
 // ---------------------------------------------------------------------------------------------
-// Full proxy map (the prior-art routing's input): s_map[bh][j][i] = q_i . Kbar_j / sqrt(d) for
+// Full proxy map (the prior-art routing's input): s_map[bh][i][j] = q_i . Kbar_j / sqrt(d) for
 // every row and block, written to memory -- the round trip the fused kernel avoids.  The same
 // fp32-accurate three-piece product as the fused kernel's routing sweep, one workgroup per
-// 128-row tile, pooled-key chunks double buffered; block-major so that a wave's 32 rows store one
-// contiguous run per block.
+// 128-row tile, pooled-key chunks double buffered.  Row-major: a wave's 32 x 32 chunk of scores is
+// transposed through LDS so that every store writes whole 128-byte row segments.
 // ---------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void proxy_map_kernel(const uint16_t* __restrict__ q,
@@ -934,6 +934,7 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_map_kernel(const uint16_t* 
   lds_u8* smem = (lds_u8*)smem_raw;
   constexpr int kChunkTile = 32 * D * 2;
   constexpr int kBuf = 3 * kChunkTile;
+  constexpr int kStageStride = 33;  // floats per staged row (33: conflict-free column writes)
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, c = lane & 31, h = lane >> 5;
   const int64_t ntiles = (N + kQTile - 1) / kQTile;
@@ -948,7 +949,8 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_map_kernel(const uint16_t* 
   const float inv_sqrt_d = 1.0f / sqrtf((float)D);
   const int64_t piece = BH * Mp * D;
   const uint16_t* kp0 = kp + bh * Mp * D;
-  float* out = smap + bh * M * N + row;
+  const int64_t row0 = tile * kQTile + wave * 32;
+  float* stage = (float*)(smem_raw + 2 * kBuf) + wave * 32 * kStageStride;  // this wave's 32 x 32
   const int nchunks = (int)(Mp / 32);
   auto issue_chunk = [&](int cb, int b) {
     lds_u8* base = smem + b * kBuf;
@@ -966,13 +968,23 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_map_kernel(const uint16_t* 
     f32x16 acc = {};
 #pragma unroll
     for (int p = 0; p < 3; ++p) acc = scores32<D>(base + p * kChunkTile, 0, qf, acc);
-    if (rvalid) {
+    // stage[r][kj] = score of row r, block kj of the chunk; then each store instruction writes
+    // two rows' 32 consecutive scores (lane l: block l % 32 of rows l / 32 + 2 i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t j = (int64_t)cb * 32 + key_of(v, h);
-        if (j < M) out[j * N] = acc[v] * inv_sqrt_d;
-      }
+    for (int v = 0; v < 16; ++v) stage[c * kStageStride + key_of(v, h)] = acc[v] * inv_sqrt_d;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int64_t j = (int64_t)cb * 32 + c;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = h + 2 * i;
+      const int64_t grow = row0 + r;
+      if (grow < N && j < M) smap[(bh * N + grow) * M + j] = stage[r * kStageStride + c];
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
@@ -1110,7 +1122,7 @@ static hipError_t launch_rowstats_t(const RowStatsArgs& a, hipStream_t stream) {
 template <int D>
 static hipError_t launch_proxy_map_t(const uint16_t* q, const uint16_t* kp, int64_t BH, int64_t N,
                                      int64_t M, int64_t Mp, float* s_map, hipStream_t stream) {
-  const size_t smem = (size_t)2 * 3 * 32 * D * 2;
+  const size_t smem = (size_t)2 * 3 * 32 * D * 2 + (size_t)4 * 32 * 33 * sizeof(float);
   auto kern = proxy_map_kernel<D>;
   hipError_t err = set_smem(kern, smem);
   if (err != hipSuccess) return err;

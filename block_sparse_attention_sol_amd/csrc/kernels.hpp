@@ -53,7 +53,7 @@ hipError_t launch_sparse(int d, const SparseArgs& a, hipStream_t stream);
 hipError_t launch_dense(int d, int64_t BH, int64_t N, const void* q, const void* k, const void* v,
                         void* out, float* lse, hipStream_t stream);
 
-// Full proxy map s_map[BH][M][N] = q . Kbar_j / sqrt(d) (fp32, block-major) from the pooled-key
+// Full proxy map s_map[BH][N][M] = q . Kbar_j / sqrt(d) (fp32, row-major) from the pooled-key
 // pieces kp [3][BH][Mp][d].
 hipError_t launch_proxy_map(int d, const uint16_t* q, const uint16_t* kp, int64_t BH, int64_t N,
                             int64_t M, int64_t Mp, float* s_map, hipStream_t stream);
@@ -61,6 +61,7 @@ hipError_t launch_proxy_map(int d, const uint16_t* q, const uint16_t* kp, int64_
 // mask [BH][N][ceil(M/32)].
 hipError_t launch_route_select(int mode, const float* s_map, int64_t BH, int64_t N, int64_t M,
                                int block, int64_t k, float p, uint32_t* mask, hipStream_t stream);
+int64_t route_max_blocks();  // largest M the selection kernel holds in registers
 
 // Matrix-core rate probe: `workgroups` x 4 waves, each issuing iters x mfma_probe_chains()
 // independent bf16 32x32x16 MFMAs.

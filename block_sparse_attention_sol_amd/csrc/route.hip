@@ -11,14 +11,13 @@
 //          decreasing order of pi (equal values: lower index first) and a block is kept while the
 //          probability of the blocks before it is below p.
 //
-// One lane per query row, 64 rows per workgroup, reading the block-major map [BH][M][N] (each
-// load instruction reads 64 consecutive rows of one block).  The k-th largest score / the
-// probability-p point is found by radix selection on an order-preserving 32-bit key of the
-// ordering value: four passes of 8 bits, each summing counts (top-k) or probabilities (top-p) of
-// the row's values under the current prefix into the lane's own 256-bin LDS histogram
-// (bins x lanes, so lanes never share a bank).  A last pass keeps every value above the selected
-// key and, among values equal to it, the lowest indices while the mass before them is below the
-// target.
+// One wave per query row.  The row's M scores (row-major map) are read once, coalesced, into
+// registers (block j in lane j % 64, slot j / 64; M <= 2048).  Both rules keep a prefix of
+// the decreasing order, so the last kept value is found by a 32-step bitwise search over an
+// order-preserving 32-bit key: the largest x with mass(key > x) >= target, where the mass counts
+// blocks (top-k, target k) or probabilities (top-p, target p * sum), summed per lane and across the
+// wave by a fixed butterfly.  The kept set is then every key above x + 1 and, among keys equal to
+// it, the lowest indices while the mass before them is below the target.
 #include <math.h>
 
 #include "common.hpp"
@@ -28,38 +27,54 @@ namespace solattn {
 
 namespace {
 
-constexpr int kRouteRows = 64;
-constexpr int kBins = 256;
+constexpr int kMaxSlots = 32;        // scores per lane: M <= 2048
+constexpr int kRowsPerGroup = 4;     // rows (waves) per workgroup
 
-// Order-preserving key of a float (larger float -> larger key; -0 taken as +0).
+// Order-preserving key of a float (larger float -> larger key; -0 taken as +0).  Every finite or
+// infinite float maps above 0.
 __device__ __forceinline__ uint32_t order_key(float x) {
   const uint32_t b = f32_bits(x == 0.f ? 0.f : x);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kRouteRows) void route_select_kernel(const float* __restrict__ smap,
-                                                                  int64_t BH, int64_t N, int64_t M,
-                                                                  int block, int64_t kk, float p,
-                                                                  uint32_t* __restrict__ mask) {
-  extern __shared__ __attribute__((aligned(16))) float hist[];  // [kBins][kRouteRows]
-  const int lane = threadIdx.x;
-  const int64_t groups = (N + kRouteRows - 1) / kRouteRows;
-  const int64_t bh = blockIdx.x / groups;
-  const int64_t row = (blockIdx.x % groups) * kRouteRows + lane;
-  const bool valid = row < N;
-  const float* col = smap + bh * M * N + (valid ? row : 0);
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+// kSlots: scores per lane (the launch picks the smallest multiple of 4 with 64 * kSlots >= M)
+template <int MODE, int kSlots>
+__global__ __launch_bounds__(64 * kRowsPerGroup) void route_select_kernel(
+    const float* __restrict__ smap, int64_t BH, int64_t N, int64_t M, int block, int64_t kk,
+    float p, uint32_t* __restrict__ mask) {
+  const int lane = threadIdx.x & 63;
+  const int64_t grow = (int64_t)blockIdx.x * kRowsPerGroup + (threadIdx.x >> 6);  // bh * N + row
+  if (grow >= BH * N) return;  // whole wave
+  const float* srow = smap + grow * M;
   const int64_t W = (M + 31) / 32;
-  uint32_t* mrow = mask + (bh * N + (valid ? row : 0)) * W;
+  uint32_t* mrow = mask + grow * W;
   const int n_last = (int)(N - (M - 1) * (int64_t)block);
   const float ln_full = logf((float)block), ln_last = logf((float)n_last);
 
-  // the ordering value of block j: s_ij (top-k) or the pooled logit s_ij + ln n_j (top-p)
-  auto value = [&](int64_t j) -> float {
-    float x = col[j * N];
-    if (MODE == 1) x += (j == M - 1) ? ln_last : ln_full;
-    return x;
-  };
+  float u[kSlots];
+  uint32_t key[kSlots];
+#pragma unroll
+  for (int r = 0; r < kSlots; ++r) {
+    const int64_t j = (int64_t)r * 64 + lane;
+    float x = -INFINITY;
+    if (j < M) {
+      x = srow[j];
+      if (MODE == 1) x += (j == M - 1) ? ln_last : ln_full;
+    }
+    u[r] = x;
+    key[r] = j < M ? order_key(x) : 0u;  // padding slots: key 0, below every real key
+  }
 
   bool all = false, none = false;
   float target = 0.f, mx = 0.f;
@@ -71,84 +86,90 @@ __global__ __launch_bounds__(kRouteRows) void route_select_kernel(const float* _
     none = !(p > 0.f);
     all = p >= 1.f;
     if (!none && !all) {
-      mx = -INFINITY;
-      for (int64_t j = 0; j < M; ++j) mx = fmaxf(mx, value(j));
+      float m = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < kSlots; ++r) m = fmaxf(m, u[r]);
+      mx = wave_max(m);
       float z = 0.f;
-      for (int64_t j = 0; j < M; ++j) z += expf(value(j) - mx);
-      target = p * z;
+#pragma unroll
+      for (int r = 0; r < kSlots; ++r) z += key[r] ? expf(u[r] - mx) : 0.f;
+      target = p * wave_sum(z);
     }
   }
-  auto weight = [&](float x) -> float { return MODE == 0 ? 1.f : expf(x - mx); };
+  float w[kSlots];
+#pragma unroll
+  for (int r = 0; r < kSlots; ++r) w[r] = key[r] == 0u ? 0.f : (MODE == 0 ? 1.f : expf(u[r] - mx));
 
-  uint32_t prefix = 0u, pmask = 0u;
-  float above = 0.f;  // mass of the values strictly above the current key range
-  if (!none && !all) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int b = 0; b < kBins; ++b) hist[b * kRouteRows + lane] = 0.f;
-      for (int64_t j = 0; j < M; ++j) {
-        const float x = value(j);
-        const uint32_t key = order_key(x);
-        if ((key & pmask) == prefix) atomicAdd(&hist[((key >> shift) & 255u) * kRouteRows + lane], weight(x));
-      }
-      // the highest bin at which the mass from the top reaches the target; if rounding leaves it
-      // short, the lowest non-empty bin (every value of the range is then kept)
-      int pick = -1;
-      float acc = above, acc_pick = above;
-      for (int b = kBins - 1; b >= 0; --b) {
-        const float hb = hist[b * kRouteRows + lane];
-        if (hb > 0.f) {
-          pick = b;
-          acc_pick = acc;
-          if (acc + hb >= target) break;
-          acc += hb;
-        }
-      }
-      if (pick < 0) pick = 0;
-      above = acc_pick;
-      prefix |= (uint32_t)pick << shift;
-      pmask |= 255u << shift;
+  uint32_t t = 0u;       // key of the last kept value
+  float above = 0.f;     // mass of the keys above t
+  if (!all && !none) {
+    uint32_t x = 0u;     // largest x with mass(key > x) >= target (x = 0 qualifies)
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t cand = x | (1u << b);
+      float m = 0.f;
+#pragma unroll
+      for (int r = 0; r < kSlots; ++r) m += key[r] > cand ? w[r] : 0.f;
+      if (wave_sum(m) >= target) x = cand;
     }
+    t = x + 1u;
+    float m = 0.f;
+#pragma unroll
+    for (int r = 0; r < kSlots; ++r) m += key[r] > t ? w[r] : 0.f;
+    above = wave_sum(m);
   }
 
-  // marking pass: above the selected key -> kept; equal -> kept in index order while the mass
-  // before them is below the target
+  // keep: above t; equal to t in index order while the mass before is below the target
   float cum = above;
-  uint32_t word = 0u;
-  for (int64_t j = 0; j < M; ++j) {
-    bool keep = all;
+#pragma unroll
+  for (int r = 0; r < kSlots; ++r) {
+    if ((int64_t)r * 64 >= M) break;
+    bool keep = all && (int64_t)r * 64 + lane < M;
     if (!all && !none) {
-      const float x = value(j);
-      const uint32_t key = order_key(x);
-      if (key > prefix) {
-        keep = true;
-      } else if (key == prefix) {
-        keep = cum < target;
-        cum += weight(x);
+      keep = key[r] > t;
+      uint64_t ties = __builtin_amdgcn_ballot_w64(key[r] == t);
+      while (ties) {  // wave-uniform loop over the equal keys of this slot, lowest lane first
+        const int l = __builtin_ctzll(ties);
+        ties &= ties - 1;
+        const float wl = __shfl(w[r], l, 64);
+        if (lane == l) keep = cum < target;
+        cum += wl;
       }
     }
-    word |= (keep ? 1u : 0u) << (j & 31);
-    if ((j & 31) == 31 || j == M - 1) {
-      if (valid) mrow[j >> 5] = word;
-      word = 0u;
-    }
+    const uint64_t bits = __builtin_amdgcn_ballot_w64(keep);
+    const int64_t w0 = (int64_t)r * 2;
+    if (lane == 0 && w0 < W) mrow[w0] = (uint32_t)bits;
+    if (lane == 1 && w0 + 1 < W) mrow[w0 + 1] = (uint32_t)(bits >> 32);
   }
+}
+
+template <int MODE, int kSlots>
+hipError_t launch_route_r(const float* s_map, int64_t BH, int64_t N, int64_t M, int block,
+                          int64_t kk, float p, uint32_t* mask, hipStream_t stream) {
+  const int64_t groups = (BH * N + kRowsPerGroup - 1) / kRowsPerGroup;
+  hipLaunchKernelGGL((route_select_kernel<MODE, kSlots>), dim3((unsigned)groups),
+                     dim3(64 * kRowsPerGroup), 0, stream, s_map, BH, N, M, block, kk, p, mask);
+  return hipGetLastError();
 }
 
 template <int MODE>
 hipError_t launch_route_t(const float* s_map, int64_t BH, int64_t N, int64_t M, int block,
                           int64_t kk, float p, uint32_t* mask, hipStream_t stream) {
-  const size_t smem = (size_t)kBins * kRouteRows * sizeof(float);
-  auto kern = route_select_kernel<MODE>;
-  hipError_t err = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  if (err != hipSuccess) return err;
-  const int64_t groups = (N + kRouteRows - 1) / kRouteRows;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(BH * groups)), dim3(kRouteRows), smem, stream, s_map,
-                     BH, N, M, block, kk, p, mask);
-  return hipGetLastError();
+  const int slots = (int)((M + 63) / 64);
+  switch ((slots + 3) / 4) {
+    case 1: return launch_route_r<MODE, 4>(s_map, BH, N, M, block, kk, p, mask, stream);
+    case 2: return launch_route_r<MODE, 8>(s_map, BH, N, M, block, kk, p, mask, stream);
+    case 3: return launch_route_r<MODE, 12>(s_map, BH, N, M, block, kk, p, mask, stream);
+    case 4: return launch_route_r<MODE, 16>(s_map, BH, N, M, block, kk, p, mask, stream);
+    case 5: return launch_route_r<MODE, 20>(s_map, BH, N, M, block, kk, p, mask, stream);
+    case 6: return launch_route_r<MODE, 24>(s_map, BH, N, M, block, kk, p, mask, stream);
+    case 7: return launch_route_r<MODE, 28>(s_map, BH, N, M, block, kk, p, mask, stream);
+    default: return launch_route_r<MODE, 32>(s_map, BH, N, M, block, kk, p, mask, stream);
+  }
 }
 
 }  // namespace
+
+int64_t route_max_blocks() { return 64 * kMaxSlots; }
 
 hipError_t launch_route_select(int mode, const float* s_map, int64_t BH, int64_t N, int64_t M,
                                int block, int64_t k, float p, uint32_t* mask, hipStream_t stream) {

@@ -219,13 +219,13 @@ def dense_fwd(q, k, v, out=None, want_lse: bool = False, stream=None):
 
 
 def proxy_map(q, k, block: int, s_map=None, workspace=None, stream=None):
-    """Full proxy map s_map [B, H, M, N] fp32 (block-major) of the prior-art routing pipeline."""
+    """Full proxy map s_map [B, H, N, M] fp32 (row-major) of the prior-art routing pipeline."""
     import torch
     lib = load_library()
     B, H, N, d = q.shape
     M = n_blocks(N, block)
     if s_map is None:
-        s_map = torch.empty((B, H, M, N), dtype=torch.float32, device=q.device)
+        s_map = torch.empty((B, H, N, M), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = new_workspace(q.shape, block, q.device)
     _check(lib.sol_proxy_map(ctypes.byref(_shape(q)), _dev(q, "q"), _dev(k, "k"), block,

@@ -126,8 +126,8 @@ int sol_dense_fwd(const sol_shape* shape, const void* q, const void* k, const vo
  * build that pipeline from the same proxy as sol_attn_fwd: map -> selection -> attention with the
  * caller's selection.
  *
- * sol_proxy_map: s_map[b][h][j][i] = q_i . Kbar_j / sqrt(d) for every query row i and key block j
- * (fp32, block-major: [B][H][M][N], B*H*M*N*4 bytes, device, written; the same fp32-accurate
+ * sol_proxy_map: s_map[b][h][i][j] = q_i . Kbar_j / sqrt(d) for every query row i and key block j
+ * (fp32, row-major: [B][H][N][M], B*H*N*M*4 bytes, device, written; the same fp32-accurate
  * values the fused kernel compares with tau).  Pools K into the workspace first (the workspace
  * of sol_attn_workspace_bytes(shape, block), contents scratch).  s_map must not overlap the
  * workspace.
@@ -139,6 +139,7 @@ int sol_proxy_map(const sol_shape* shape, const void* q, const void* k, int bloc
  * Top-k selection from s_map: for each row, the k blocks with the largest s_ij, equal scores
  * keeping the lower block index first.  k <= 0 keeps none, k >= M keeps all.
  *   mask  [B][H][N][ceil(M/32)] uint32, device, written (bit j%32 of word j/32 = block j kept).
+ * A row's scores are held in registers: M <= 2048 (else SOL_EUNSUPPORTED).
  */
 int sol_select_topk(const sol_shape* shape, int block, const float* s_map, int64_t k,
                     uint32_t* mask, void* stream);

@@ -188,3 +188,10 @@ def test_routing_entries_reject(lib):
     assert lib.sol_select_topp(ctypes.byref(s), 128, smap, nan, mask, None) == solattn.SOL_EINVAL
     assert lib.sol_select_topp(ctypes.byref(s), 128, None, 0.5, mask, None) == solattn.SOL_EINVAL
     assert lib.sol_select_topp(ctypes.byref(s), 128, smap, 0.5, smap, None) == solattn.SOL_EINVAL
+
+
+def test_selection_block_limit(lib):
+    s = solattn.SolShape(1, 1, 2049 * 64, 64)  # M = 2049 key blocks per row
+    smap, mask = _ptrs(2)
+    assert lib.sol_select_topk(ctypes.byref(s), 64, smap, 3, mask, None) == solattn.SOL_EUNSUPPORTED
+    assert b"2048" in lib.sol_last_error()

@@ -70,12 +70,12 @@ def test_proxy_map(sol, B, H, N, d, block):
     smap = sol.proxy_map(q, k, block)
     torch.cuda.synchronize()
     M = oracle.n_blocks(N, block)
-    assert smap.shape == (B, H, M, N)
+    assert smap.shape == (B, H, N, M)
     for b in range(B):
         for h in range(H):
             r = oracle.attn_rows(_np(q[b, h]), _np(k[b, h]), _np(v[b, h]), 0.0, block, want_s=True)
             s = r["s"]                                   # [N, M]
-            g = _np(smap[b, h]).T.astype(np.float64)     # [N, M]
+            g = _np(smap[b, h]).astype(np.float64)       # [N, M]
             err = float(np.abs(g - s).max())
             assert err <= 1e-5 * max(1.0, float(np.abs(s).max())), (b, h, err)
 
