@@ -94,6 +94,50 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
+solattn::Strides contiguous(const sol_shape& s) {
+  return solattn::Strides::contiguous(s.H, s.N, s.d);
+}
+
+solattn::Strides to_strides(const sol_shape& s, const sol_strides* st) {
+  if (!st) return contiguous(s);
+  return solattn::Strides{s.H, st->b, st->h, st->n};
+}
+
+// Bytes from the first element of a strided [B][H][N][d] bf16 view to the end of its last row.
+size_t extent_bytes(const sol_shape& s, const solattn::Strides& st) {
+  return (size_t)((s.B - 1) * st.sb + (s.H - 1) * st.sh + (s.N - 1) * st.sn + s.d) * 2;
+}
+
+// Strides the kernels accept: non-negative, multiples of 8 elements (16-byte aligned rows), rows
+// at least d apart and within the copies' 32-bit per-lane offsets; for an output (writable)
+// also no two elements at one address: sorted by stride, every dimension of size > 1 must step
+// past the whole extent of the dimensions inside it.
+int check_strides(const sol_shape& s, const sol_strides* st, const char* name, bool writable) {
+  if (!st) return SOL_OK;
+  const int64_t v[3] = {st->b, st->h, st->n};
+  for (int64_t x : v)
+    if (x < 0 || (x & 7)) return fail(SOL_EINVAL, "%s strides must be non-negative multiples of 8", name);
+  if (st->n < s.d) return fail(SOL_EINVAL, "%s token stride %lld is below d", name, (long long)st->n);
+  if (st->n > (int64_t(1) << 23)) return fail(SOL_EUNSUPPORTED, "%s token stride too large", name);
+  if (writable) {
+    int64_t dims[3][2] = {{st->n, s.N}, {st->h, s.H}, {st->b, s.B}};
+    for (int i = 0; i < 3; ++i)  // sort by stride
+      for (int j = i + 1; j < 3; ++j)
+        if (dims[j][0] < dims[i][0]) {
+          int64_t t0 = dims[i][0], t1 = dims[i][1];
+          dims[i][0] = dims[j][0]; dims[i][1] = dims[j][1];
+          dims[j][0] = t0; dims[j][1] = t1;
+        }
+    int64_t inner = s.d;  // extent covered by the dimensions inside
+    for (int i = 0; i < 3; ++i) {
+      if (dims[i][1] == 1) continue;
+      if (dims[i][0] < inner) return fail(SOL_EINVAL, "%s strides make elements overlap", name);
+      inner = dims[i][0] * (dims[i][1] - 1) + inner;
+    }
+  }
+  return SOL_OK;
+}
+
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(SOL_EHIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -143,8 +187,9 @@ int sol_pool_kv(const sol_shape* shape, const void* k, const void* v, int block,
   const int64_t M = n_blocks(shape->N, block);
   const size_t pooled = (size_t)(BH * M * shape->d) * sizeof(float);
   if (overlaps(kbar, pooled, vbar, pooled)) return fail(SOL_EINVAL, "kbar and vbar overlap");
-  return hip_status(solattn::launch_pool((int)shape->d, BH, shape->N, block, k, v, kbar, vbar,
-                                         nullptr, nullptr, 0, (hipStream_t)stream),
+  return hip_status(solattn::launch_pool((int)shape->d, BH, shape->N, block, k, v,
+                                         contiguous(*shape), kbar, vbar, nullptr, nullptr, 0,
+                                         (hipStream_t)stream),
                     "pool kernel launch");
 }
 
@@ -152,11 +197,16 @@ namespace {
 
 // sol_attn_fwd_ex and sol_attn_fwd_masked: with mask_in the caller's selection replaces the
 // threshold (no row statistics are computed) and `drop` comes from the argument.
-int attn_forward(const sol_shape* shape, const void* q, const void* k, const void* v, float beta,
-                 int block, void* out, void* workspace, size_t workspace_bytes,
-                 const sol_attn_debug* dbg, const uint32_t* mask_in, int drop_in, void* stream) {
+int attn_forward(const sol_shape* shape, const sol_strides* in_st, const sol_strides* out_st,
+                 const void* q, const void* k, const void* v, float beta, int block, void* out,
+                 void* workspace, size_t workspace_bytes, const sol_attn_debug* dbg,
+                 const uint32_t* mask_in, int drop_in, void* stream) {
   int st;
   if ((st = check_shape(shape)) || (st = check_block(block))) return st;
+  if ((st = check_strides(*shape, in_st, "input", false)) ||
+      (st = check_strides(*shape, out_st, "output", true)))
+    return st;
+  const solattn::Strides ins = to_strides(*shape, in_st), outs = to_strides(*shape, out_st);
   if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
       (st = check_tensor(out, "out")))
     return st;
@@ -167,9 +217,9 @@ int attn_forward(const sol_shape* shape, const void* q, const void* k, const voi
   if (!aligned16(workspace)) return fail(SOL_EINVAL, "workspace is not 16-byte aligned");
   if (workspace_bytes < w.total)
     return fail(SOL_EWORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, w.total);
-  const size_t tensor = (size_t)(shape->B * shape->H * shape->N * shape->d) * 2;
-  if (overlaps(out, tensor, q, tensor) || overlaps(out, tensor, k, tensor) ||
-      overlaps(out, tensor, v, tensor) || overlaps(out, tensor, workspace, w.total))
+  const size_t ein = extent_bytes(*shape, ins), eout = extent_bytes(*shape, outs);
+  if (overlaps(out, eout, q, ein) || overlaps(out, eout, k, ein) || overlaps(out, eout, v, ein) ||
+      overlaps(out, eout, workspace, w.total))
     return fail(SOL_EINVAL, "out overlaps an input or the workspace");
   if (dbg) {
     const void* opt[] = {dbg->mask, dbg->mu,  dbg->sigma,    dbg->tau,
@@ -201,7 +251,7 @@ int attn_forward(const sol_shape* shape, const void* q, const void* k, const voi
   };
   hipError_t e = mark(0);
   if (e != hipSuccess) return hip_status(e, "event record");
-  e = solattn::launch_pool(d, BH, shape->N, block, k, v, kbar, nullptr, kp, vbt, Mp, s);
+  e = solattn::launch_pool(d, BH, shape->N, block, k, v, ins, kbar, nullptr, kp, vbt, Mp, s);
   if (e != hipSuccess) return hip_status(e, "pool kernel launch");
   if ((e = mark(1)) != hipSuccess) return hip_status(e, "event record");
   if (!mask_in) {
@@ -209,6 +259,7 @@ int attn_forward(const sol_shape* shape, const void* q, const void* k, const voi
     if (e != hipSuccess) return hip_status(e, "pooled-key statistics launch");
     solattn::RowStatsArgs r{};
     r.q = (const uint16_t*)q;
+    r.qs = ins;
     r.cp = cp;
     r.kglob = kglob;
     r.BH = BH;
@@ -230,6 +281,8 @@ int attn_forward(const sol_shape* shape, const void* q, const void* k, const voi
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;
   a.out = (uint16_t*)out;
+  a.in = ins;
+  a.outs = outs;
   a.kp = kp;
   a.vbt = vbt;
   a.tau = tau;
@@ -258,16 +311,24 @@ int attn_forward(const sol_shape* shape, const void* q, const void* k, const voi
 int sol_attn_fwd_ex(const sol_shape* shape, const void* q, const void* k, const void* v,
                     float beta, int block, void* out, void* workspace, size_t workspace_bytes,
                     const sol_attn_debug* dbg, void* stream) {
-  return attn_forward(shape, q, k, v, beta, block, out, workspace, workspace_bytes, dbg, nullptr, 0,
-                      stream);
+  return attn_forward(shape, nullptr, nullptr, q, k, v, beta, block, out, workspace,
+                      workspace_bytes, dbg, nullptr, 0, stream);
+}
+
+int sol_attn_fwd_strided(const sol_shape* shape, const sol_strides* in_strides,
+                         const sol_strides* out_strides, const void* q, const void* k,
+                         const void* v, float beta, int block, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return attn_forward(shape, in_strides, out_strides, q, k, v, beta, block, out, workspace,
+                      workspace_bytes, nullptr, nullptr, 0, stream);
 }
 
 int sol_attn_fwd_masked(const sol_shape* shape, const void* q, const void* k, const void* v,
                         const uint32_t* mask, int block, int drop_unselected, void* out,
                         void* workspace, size_t workspace_bytes, void* stream) {
   if (!mask) return fail(SOL_EINVAL, "mask is NULL");
-  return attn_forward(shape, q, k, v, 0.f, block, out, workspace, workspace_bytes, nullptr, mask,
-                      drop_unselected ? 1 : 0, stream);
+  return attn_forward(shape, nullptr, nullptr, q, k, v, 0.f, block, out, workspace,
+                      workspace_bytes, nullptr, mask, drop_unselected ? 1 : 0, stream);
 }
 
 int sol_proxy_map(const sol_shape* shape, const void* q, const void* k, int block, float* s_map,
@@ -289,10 +350,12 @@ int sol_proxy_map(const sol_shape* shape, const void* q, const void* k, int bloc
     return fail(SOL_EINVAL, "s_map overlaps the workspace");
   unsigned char* ws = (unsigned char*)workspace;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = solattn::launch_pool((int)shape->d, BH, shape->N, block, k, k, (float*)(ws + w.kbar),
-                                      nullptr, (uint16_t*)(ws + w.kp), (uint16_t*)(ws + w.vbt), Mp, s);
+  const solattn::Strides cs = contiguous(*shape);
+  hipError_t e = solattn::launch_pool((int)shape->d, BH, shape->N, block, k, k, cs,
+                                      (float*)(ws + w.kbar), nullptr, (uint16_t*)(ws + w.kp),
+                                      (uint16_t*)(ws + w.vbt), Mp, s);
   if (e != hipSuccess) return hip_status(e, "pool kernel launch");
-  return hip_status(solattn::launch_proxy_map((int)shape->d, (const uint16_t*)q,
+  return hip_status(solattn::launch_proxy_map((int)shape->d, (const uint16_t*)q, cs,
                                               (const uint16_t*)(ws + w.kp), BH, shape->N, M, Mp,
                                               s_map, s),
                     "proxy map kernel launch");
@@ -339,21 +402,30 @@ int sol_attn_fwd(const sol_shape* shape, const void* q, const void* k, const voi
                          stream);
 }
 
-int sol_dense_fwd(const sol_shape* shape, const void* q, const void* k, const void* v, void* out,
-                  float* lse, void* stream) {
+int sol_dense_fwd_strided(const sol_shape* shape, const sol_strides* in_strides,
+                          const sol_strides* out_strides, const void* q, const void* k,
+                          const void* v, void* out, float* lse, void* stream) {
   int st;
   if ((st = check_shape(shape))) return st;
+  if ((st = check_strides(*shape, in_strides, "input", false)) ||
+      (st = check_strides(*shape, out_strides, "output", true)))
+    return st;
   if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
       (st = check_tensor(out, "out")))
     return st;
   if (lse && ((uintptr_t)lse & 3u)) return fail(SOL_EINVAL, "lse not 4-byte aligned");
-  const size_t tensor = (size_t)(shape->B * shape->H * shape->N * shape->d) * 2;
-  if (overlaps(out, tensor, q, tensor) || overlaps(out, tensor, k, tensor) ||
-      overlaps(out, tensor, v, tensor))
+  const solattn::Strides ins = to_strides(*shape, in_strides), outs = to_strides(*shape, out_strides);
+  const size_t ein = extent_bytes(*shape, ins), eout = extent_bytes(*shape, outs);
+  if (overlaps(out, eout, q, ein) || overlaps(out, eout, k, ein) || overlaps(out, eout, v, ein))
     return fail(SOL_EINVAL, "out overlaps an input");
-  return hip_status(solattn::launch_dense((int)shape->d, shape->B * shape->H, shape->N, q, k, v,
-                                          out, lse, (hipStream_t)stream),
+  return hip_status(solattn::launch_dense((int)shape->d, shape->B * shape->H, shape->N, q, k, v, ins,
+                                          out, outs, lse, (hipStream_t)stream),
                     "dense attention kernel launch");
+}
+
+int sol_dense_fwd(const sol_shape* shape, const void* q, const void* k, const void* v, void* out,
+                  float* lse, void* stream) {
+  return sol_dense_fwd_strided(shape, nullptr, nullptr, q, k, v, out, lse, stream);
 }
 
 }  // extern "C"

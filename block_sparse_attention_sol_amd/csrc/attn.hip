@@ -104,18 +104,19 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
   return r;
 }
 
-// Per-lane byte offsets, within a ROWS-row tile of a row-major [*, D] bf16 matrix, of the 16 bytes
-// each lane copies so that the LDS tile comes out swizzled (see load_tile).
+// Per-lane byte offsets, within a ROWS-row tile of a bf16 matrix with rows of D contiguous
+// elements sn elements apart, of the 16 bytes each lane copies so that the LDS tile comes out
+// swizzled (see load_tile).
 template <int D, int ROWS>
 struct TileOffsets {
   uint32_t v[tile_loads<D, ROWS>()];
-  __device__ __forceinline__ TileOffsets() {
+  __device__ __forceinline__ explicit TileOffsets(int64_t sn) {
     constexpr int kChunks = D / 8;
 #pragma unroll
     for (int i = 0; i < tile_loads<D, ROWS>(); ++i) {
       const int p = i * kThreads + (int)threadIdx.x;
       const int row = p / kChunks;
-      v[i] = (uint32_t)(row * D * 2 + swz<D>(row, p % kChunks) * 16);
+      v[i] = (uint32_t)(row * sn * 2 + swz<D>(row, p % kChunks) * 16);
     }
   }
 };
@@ -158,6 +159,17 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Rows [r0, r0 + ROWS) of a row-strided bf16 matrix (row r at base + r * sn, rows below `limit`)
+// into an LDS tile; rows at or beyond `limit` read as zeros (the buffer ends after the last valid
+// row, and every later row starts at or beyond that end since sn >= D).
+template <int D, int ROWS>
+__device__ __forceinline__ void load_rows(const uint16_t* base, int64_t r0, int64_t limit, int64_t sn,
+                                          const TileOffsets<D, ROWS>& off, lds_u8* tile) {
+  const int64_t n = limit - r0 < ROWS ? limit - r0 : ROWS;
+  const uint32_t bytes = (uint32_t)((n - 1) * sn * 2 + D * 2);
+  load_tile_buf<D, ROWS>(make_rsrc(base + r0 * sn, bytes), 0u, off, tile);
 }
 
 // Workgroup barrier without the memory fence of __syncthreads: the pipelined loops order their
@@ -507,8 +519,8 @@ __device__ __forceinline__ void load_q(const uint16_t* __restrict__ qrow, bool v
 template <int D>
 __device__ __forceinline__ void epilogue(const f32x16 (&o)[D / 32], float mrun, float lsum,
                                          int64_t row0, int64_t N, uint16_t* __restrict__ out,
-                                         float* __restrict__ out_f32, float* __restrict__ lse,
-                                         lds_u8* stage) {
+                                         int64_t on, float* __restrict__ out_f32,
+                                         float* __restrict__ lse, lds_u8* stage) {
   const int lane = threadIdx.x & 63;
   const int c = lane & 31, h = lane >> 5;
   const int64_t row = row0 + c;
@@ -539,7 +551,7 @@ __device__ __forceinline__ void epilogue(const f32x16 (&o)[D / 32], float mrun, 
     const int idx = i * 64 + lane;
     const int r = idx / kChunks, ch = idx % kChunks;
     const u32x4 v = lds_read16(stage + tile_off<D>(r, ch));
-    if (row0 + r < N) *reinterpret_cast<u32x4*>(out + (row0 + r) * D + ch * 8) = v;
+    if (row0 + r < N) *reinterpret_cast<u32x4*>(out + (row0 + r) * on + ch * 8) = v;
   }
 }
 
@@ -584,7 +596,7 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(RowStatsArgs a) {
     if (tile >= ntiles) break;
     const int64_t row = tile * kQTile + wave * 32 + c;
     const bool valid = row < a.N;
-    const uint16_t* qrow = a.q + (bh * a.N + row) * D;
+    const uint16_t* qrow = a.q + a.qs.base(bh) + row * a.qs.sn;
     bf16x8 qf[D / 16];
     load_q<D>(qrow, valid, qf);
     // query values in the layout of C q's rows (a = 32 ab + 8 g + 4 h + 0..3)
@@ -667,13 +679,14 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
   const int64_t row = row0 + c;
   const bool rvalid = row < a.N;
 
-  const uint16_t* qb = a.q + bh * a.N * D;
-  const uint16_t* kb = a.k + bh * a.N * D;
-  const uint16_t* vb = a.v + bh * a.N * D;
+  const uint16_t* qb = a.q + a.in.base(bh);
+  const uint16_t* kb = a.k + a.in.base(bh);
+  const uint16_t* vb = a.v + a.in.base(bh);
+  const int64_t sn = a.in.sn;
   uint32_t* rmask = a.rowmask + bh * W * a.N;  // word w of row r at rmask[w * N + r]
 
   bf16x8 qf[D / 16];
-  load_q<D>(qb + row * D, rvalid, qf);
+  load_q<D>(qb + row * sn, rvalid, qf);
   // padding rows keep nothing; with a caller's selection the threshold is not used
   const float tau = (rvalid && !a.mask_in) ? a.tau[bh * a.N + row] : INFINITY;
   // s >= tau  <=>  raw dot product >= tau * sqrt(d)  (compared in fp32)
@@ -803,13 +816,12 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
       it_s = -1;
     }
   };
-  const TileOffsets<D, kStage> toff;
+  const TileOffsets<D, kStage> toff(sn);
   auto issue = [&](int j, int s, int buf) {
-    const int r0 = j * BLK + s * kStage;
-    const uint32_t bytes = (uint32_t)((int)a.N - r0) * (uint32_t)(D * 2);
+    const int64_t r0 = (int64_t)j * BLK + s * kStage;
     lds_u8* base = smem + buf * kStageBytes;
-    load_tile_buf<D, kStage>(make_rsrc(kb + (int64_t)r0 * D, bytes), 0u, toff, base);
-    load_tile_buf<D, kStage>(make_rsrc(vb + (int64_t)r0 * D, bytes), 0u, toff, base + kTileBytes);
+    load_rows<D, kStage>(kb, r0, a.N, sn, toff, base);
+    load_rows<D, kStage>(vb, r0, a.N, sn, toff, base + kTileBytes);
   };
 
   // One barrier per stage: it publishes the stage's copy (each lane waited for its own loads)
@@ -863,7 +875,7 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
   if (a.tile_kept && t == 0) a.tile_kept[bh * ntiles + tile] = kept_blocks;
   bar();  // every wave is done with the stage buffers before the epilogue reuses them
 
-  epilogue<D>(o, mrun, lsum, row0, a.N, a.out + bh * a.N * D,
+  epilogue<D>(o, mrun, lsum, row0, a.N, a.out + a.outs.base(bh), a.outs.sn,
               a.out_f32 ? a.out_f32 + bh * a.N * D : nullptr, a.lse ? a.lse + bh * a.N : nullptr,
               smem + wave * 32 * D * 2);
 }
@@ -874,17 +886,15 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
 // Copies are issued K0, V0, K1 (prologue), then V_{n+1} at half 0 and K_{n+2} at half 1 of stage n.
 template <int D, int B, int HB, bool NEXT>
 __device__ __forceinline__ void dense_half(int n, int nst, int64_t N, const uint16_t* kb,
-                                           const uint16_t* vb, lds_u8* kbuf, lds_u8* vbuf,
-                                           const TileOffsets<D, kStage>& toff,
+                                           const uint16_t* vb, int64_t rs, lds_u8* kbuf,
+                                           lds_u8* vbuf, const TileOffsets<D, kStage>& toff,
                                            const bf16x8 (&qf)[D / 16], float sl2,
                                            const f32x16& sc, f32x16& sn, float& mrun,
                                            float& lsum, f32x16 (&o)[D / 32]) {
   constexpr int kTileBytes = kStage * D * 2;
   constexpr int L = tile_loads<D, kStage>();
   auto issue = [&](const uint16_t* src, int st, lds_u8* dst) {
-    const int r0 = st * kStage;
-    const uint32_t bytes = (uint32_t)((int)N - r0) * (uint32_t)(D * 2);
-    load_tile_buf<D, kStage>(make_rsrc(src + (int64_t)r0 * D, bytes), 0u, toff, dst);
+    load_rows<D, kStage>(src, (int64_t)st * kStage, N, rs, toff, dst);
   };
   const bool more = n + 1 < nst;
   if constexpr (HB == 0) {
@@ -927,6 +937,7 @@ __device__ __forceinline__ void dense_half(int n, int nst, int64_t N, const uint
 // ---------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void proxy_map_kernel(const uint16_t* __restrict__ q,
+                                                                Strides qs,
                                                                 const uint16_t* __restrict__ kp,
                                                                 int64_t BH, int64_t N, int64_t M,
                                                                 int64_t Mp, float* __restrict__ smap) {
@@ -945,7 +956,7 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_map_kernel(const uint16_t* 
   const int64_t row = tile * kQTile + wave * 32 + c;
   const bool rvalid = row < N;
   bf16x8 qf[D / 16];
-  load_q<D>(q + (bh * N + row) * D, rvalid, qf);
+  load_q<D>(q + qs.base(bh) + row * qs.sn, rvalid, qf);
   const float inv_sqrt_d = 1.0f / sqrtf((float)D);
   const int64_t piece = BH * Mp * D;
   const uint16_t* kp0 = kp + bh * Mp * D;
@@ -996,7 +1007,9 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void dense_attn_kernel(const uint16_t* __restrict__ q,
                                                                  const uint16_t* __restrict__ k,
                                                                  const uint16_t* __restrict__ v,
+                                                                 Strides in,
                                                                  uint16_t* __restrict__ out,
+                                                                 Strides outs,
                                                                  float* __restrict__ lse,
                                                                  int64_t BH, int64_t N) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -1012,11 +1025,12 @@ __global__ __launch_bounds__(kThreads, 2) void dense_attn_kernel(const uint16_t*
   const int64_t row0 = tile * kQTile + wave * 32;
   const int64_t row = row0 + c;
   const bool rvalid = row < N;
-  const uint16_t* kb = k + bh * N * D;
-  const uint16_t* vb = v + bh * N * D;
+  const uint16_t* kb = k + in.base(bh);
+  const uint16_t* vb = v + in.base(bh);
+  const int64_t sn = in.sn;
 
   bf16x8 qf[D / 16];
-  load_q<D>(q + (bh * N + row) * D, rvalid, qf);
+  load_q<D>(q + in.base(bh) + row * sn, rvalid, qf);
   const float sl2 = kLog2e / sqrtf((float)D);
   f32x16 o[D / 32];
 #pragma unroll
@@ -1024,13 +1038,11 @@ __global__ __launch_bounds__(kThreads, 2) void dense_attn_kernel(const uint16_t*
   float mrun = -1e30f, lsum = 0.f;
 
   const int nst = (int)((N + kStage - 1) / kStage);
-  const TileOffsets<D, kStage> toff;
+  const TileOffsets<D, kStage> toff(sn);
   lds_u8* kbuf = smem;                        // K tiles: kbuf + b * kTileBytes
   lds_u8* vbuf = smem + 2 * kTileBytes;       // V tiles
   auto issue = [&](const uint16_t* src, int st, lds_u8* dst) {
-    const int r0 = st * kStage;
-    const uint32_t bytes = (uint32_t)((int)N - r0) * (uint32_t)(D * 2);
-    load_tile_buf<D, kStage>(make_rsrc(src + (int64_t)r0 * D, bytes), 0u, toff, dst);
+    load_rows<D, kStage>(src, (int64_t)st * kStage, N, sn, toff, dst);
   };
 
   // prologue: K0, V0, K1 in LDS; scores and max of the first 32 keys
@@ -1051,22 +1063,23 @@ __global__ __launch_bounds__(kThreads, 2) void dense_attn_kernel(const uint16_t*
   // next block
   int n = 0;
   for (; n + 2 < nst; n += 2) {
-    dense_half<D, 0, 0, true>(n, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
-    dense_half<D, 0, 1, true>(n, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
-    dense_half<D, 1, 0, true>(n + 1, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
-    dense_half<D, 1, 1, true>(n + 1, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
+    dense_half<D, 0, 0, true>(n, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
+    dense_half<D, 0, 1, true>(n, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
+    dense_half<D, 1, 0, true>(n + 1, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
+    dense_half<D, 1, 1, true>(n + 1, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
   }
   if (n + 1 < nst) {
-    dense_half<D, 0, 0, true>(n, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
-    dense_half<D, 0, 1, true>(n, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
-    dense_half<D, 1, 0, true>(n + 1, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
-    dense_half<D, 1, 1, false>(n + 1, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
+    dense_half<D, 0, 0, true>(n, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
+    dense_half<D, 0, 1, true>(n, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
+    dense_half<D, 1, 0, true>(n + 1, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
+    dense_half<D, 1, 1, false>(n + 1, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
   } else {
-    dense_half<D, 0, 0, true>(n, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
-    dense_half<D, 0, 1, false>(n, nst, N, kb, vb, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
+    dense_half<D, 0, 0, true>(n, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
+    dense_half<D, 0, 1, false>(n, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
   }
   bar();  // stage buffers free for the epilogue
-  epilogue<D>(o, mrun, lsum, row0, N, out + bh * N * D, nullptr, lse ? lse + bh * N : nullptr,
+  epilogue<D>(o, mrun, lsum, row0, N, out + outs.base(bh), outs.sn, nullptr,
+              lse ? lse + bh * N : nullptr,
               smem + wave * 32 * D * 2);
 }
 
@@ -1120,22 +1133,24 @@ static hipError_t launch_rowstats_t(const RowStatsArgs& a, hipStream_t stream) {
 }
 
 template <int D>
-static hipError_t launch_proxy_map_t(const uint16_t* q, const uint16_t* kp, int64_t BH, int64_t N,
-                                     int64_t M, int64_t Mp, float* s_map, hipStream_t stream) {
+static hipError_t launch_proxy_map_t(const uint16_t* q, const Strides& qs, const uint16_t* kp,
+                                     int64_t BH, int64_t N, int64_t M, int64_t Mp, float* s_map,
+                                     hipStream_t stream) {
   const size_t smem = (size_t)2 * 3 * 32 * D * 2 + (size_t)4 * 32 * 33 * sizeof(float);
   auto kern = proxy_map_kernel<D>;
   hipError_t err = set_smem(kern, smem);
   if (err != hipSuccess) return err;
   const int64_t ntiles = (N + kQTile - 1) / kQTile;
-  hipLaunchKernelGGL(kern, dim3(xcd_grid(BH * ntiles)), dim3(kThreads), smem, stream, q, kp, BH, N,
-                     M, Mp, s_map);
+  hipLaunchKernelGGL(kern, dim3(xcd_grid(BH * ntiles)), dim3(kThreads), smem, stream, q, qs, kp, BH,
+                     N, M, Mp, s_map);
   return hipGetLastError();
 }
 
-hipError_t launch_proxy_map(int d, const uint16_t* q, const uint16_t* kp, int64_t BH, int64_t N,
-                            int64_t M, int64_t Mp, float* s_map, hipStream_t stream) {
-  return d == 64 ? launch_proxy_map_t<64>(q, kp, BH, N, M, Mp, s_map, stream)
-                 : launch_proxy_map_t<128>(q, kp, BH, N, M, Mp, s_map, stream);
+hipError_t launch_proxy_map(int d, const uint16_t* q, const Strides& qs, const uint16_t* kp,
+                            int64_t BH, int64_t N, int64_t M, int64_t Mp, float* s_map,
+                            hipStream_t stream) {
+  return d == 64 ? launch_proxy_map_t<64>(q, qs, kp, BH, N, M, Mp, s_map, stream)
+                 : launch_proxy_map_t<128>(q, qs, kp, BH, N, M, Mp, s_map, stream);
 }
 
 hipError_t launch_rowstats(int d, const RowStatsArgs& a, hipStream_t stream) {
@@ -1144,22 +1159,24 @@ hipError_t launch_rowstats(int d, const RowStatsArgs& a, hipStream_t stream) {
 
 template <int D>
 static hipError_t launch_dense_t(int64_t BH, int64_t N, const void* q, const void* k,
-                                 const void* v, void* out, float* lse, hipStream_t stream) {
+                                 const void* v, const Strides& in, void* out, const Strides& outs,
+                                 float* lse, hipStream_t stream) {
   const size_t smem = (size_t)4 * kStage * D * 2;
   auto kern = dense_attn_kernel<D>;
   hipError_t err = set_smem(kern, smem);
   if (err != hipSuccess) return err;
   const int64_t ntiles = (N + kQTile - 1) / kQTile;
   hipLaunchKernelGGL(kern, dim3(xcd_grid(BH * ntiles)), dim3(kThreads), smem, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)out,
-                     lse, BH, N);
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, in,
+                     (uint16_t*)out, outs, lse, BH, N);
   return hipGetLastError();
 }
 
 hipError_t launch_dense(int d, int64_t BH, int64_t N, const void* q, const void* k, const void* v,
-                        void* out, float* lse, hipStream_t stream) {
-  return d == 64 ? launch_dense_t<64>(BH, N, q, k, v, out, lse, stream)
-                 : launch_dense_t<128>(BH, N, q, k, v, out, lse, stream);
+                        const Strides& in, void* out, const Strides& outs, float* lse,
+                        hipStream_t stream) {
+  return d == 64 ? launch_dense_t<64>(BH, N, q, k, v, in, out, outs, lse, stream)
+                 : launch_dense_t<128>(BH, N, q, k, v, in, out, outs, lse, stream);
 }
 
 }  // namespace solattn

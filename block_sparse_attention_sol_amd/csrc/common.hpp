@@ -58,6 +58,14 @@ __device__ __forceinline__ float add_bf16x2(uint32_t packed, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
 }
 
+// Element strides of a [B][H][N][d] bf16 view whose d elements are contiguous: the start of row
+// n of head (b, h) is b * sb + h * sh + n * sn.  The kernels take the combined index bh = b*H + h.
+struct Strides {
+  int64_t H, sb, sh, sn;
+  __host__ __device__ int64_t base(int64_t bh) const { return (bh / H) * sb + (bh % H) * sh; }
+  static Strides contiguous(int64_t H, int64_t N, int64_t d) { return Strides{H, H * N * d, N * d, d}; }
+};
+
 // Lane-pair combines across the two halves of the wave (lane l with lane l ^ 32), with the
 // gfx950 v_permlane32_swap (a VALU op, no LDS round trip).  Swapping a register with itself
 // leaves lanes 0-31 of the first result and lanes 32-63 of the second holding x, the other

@@ -4,19 +4,22 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.hpp"
+
 namespace solattn {
 
 // Pooled K/V of every key block.  kp / vbt (and Mp) only for the attention workspace; NULL in
 // the public pooling call.
 hipError_t launch_pool(int d, int64_t BH, int64_t N, int block, const void* k, const void* v,
-                       float* kbar, float* vbar, uint16_t* kp, uint16_t* vbt, int64_t Mp,
-                       hipStream_t stream);
+                       const Strides& kv, float* kbar, float* vbar, uint16_t* kp, uint16_t* vbt,
+                       int64_t Mp, hipStream_t stream);
 // Mean (fp32 and fp64) and covariance (three bf16 pieces) of the pooled keys of every head.
 hipError_t launch_kstats(int d, int64_t BH, int64_t M, const float* kbar, float* kglob,
                          double* kglob64, uint16_t* cp, hipStream_t stream);
 
 struct RowStatsArgs {
   const uint16_t* q;
+  Strides qs;
   const uint16_t* cp;     // [3][BH][d][d] covariance pieces (hi, mid, lo)
   const float* kglob;     // [BH][d]
   int64_t BH, N;
@@ -33,6 +36,8 @@ struct SparseArgs {
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* out;
+  Strides in;           // q, k, v
+  Strides outs;         // out
   const uint16_t* kp;   // [3][BH][Mp][d] pooled keys (hi, mid, lo)
   const uint16_t* vbt;  // [BH][d][Mp] pooled values, transposed
   const float* tau;     // [BH][N]
@@ -51,12 +56,14 @@ struct SparseArgs {
 hipError_t launch_sparse(int d, const SparseArgs& a, hipStream_t stream);
 
 hipError_t launch_dense(int d, int64_t BH, int64_t N, const void* q, const void* k, const void* v,
-                        void* out, float* lse, hipStream_t stream);
+                        const Strides& in, void* out, const Strides& outs, float* lse,
+                        hipStream_t stream);
 
 // Full proxy map s_map[BH][N][M] = q . Kbar_j / sqrt(d) (fp32, row-major) from the pooled-key
 // pieces kp [3][BH][Mp][d].
-hipError_t launch_proxy_map(int d, const uint16_t* q, const uint16_t* kp, int64_t BH, int64_t N,
-                            int64_t M, int64_t Mp, float* s_map, hipStream_t stream);
+hipError_t launch_proxy_map(int d, const uint16_t* q, const Strides& qs, const uint16_t* kp,
+                            int64_t BH, int64_t N, int64_t M, int64_t Mp, float* s_map,
+                            hipStream_t stream);
 // Top-k (mode 0, count k) or top-p (mode 1, probability p) selection per row from s_map, written as
 // mask [BH][N][ceil(M/32)].
 hipError_t launch_route_select(int mode, const float* s_map, int64_t BH, int64_t N, int64_t M,

@@ -24,9 +24,9 @@ namespace solattn {
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void pool_kv_kernel(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t N, int block, int64_t M,
-    int64_t Mp, float* __restrict__ kbar, float* __restrict__ vbar, uint16_t* __restrict__ kp,
-    uint16_t* __restrict__ vbt) {
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, Strides kv, int64_t N, int block,
+    int64_t M, int64_t Mp, float* __restrict__ kbar, float* __restrict__ vbar,
+    uint16_t* __restrict__ kp, uint16_t* __restrict__ vbt) {
   constexpr int kChunks = D / 8;               // 16-byte chunks per row
   constexpr int kGroups = kThreads / kChunks;  // row groups
   __shared__ float part[2][kGroups][D];
@@ -49,15 +49,15 @@ __global__ __launch_bounds__(kThreads) void pool_kv_kernel(
 
   const int64_t lo = j * (int64_t)block;
   const int64_t hi = (lo + block < N) ? lo + block : N;
-  const uint16_t* kb = k + bh * N * D;
-  const uint16_t* vb = v + bh * N * D;
+  const uint16_t* kb = k + kv.base(bh);
+  const uint16_t* vb = v + kv.base(bh);
 
   float sk[8], sv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) sk[e] = sv[e] = 0.f;
   for (int64_t r = lo + rg; r < hi; r += kGroups) {
-    u32x4 a = *reinterpret_cast<const u32x4*>(kb + r * D + cc * 8);
-    u32x4 b = *reinterpret_cast<const u32x4*>(vb + r * D + cc * 8);
+    u32x4 a = *reinterpret_cast<const u32x4*>(kb + r * kv.sn + cc * 8);
+    u32x4 b = *reinterpret_cast<const u32x4*>(vb + r * kv.sn + cc * 8);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       sk[2 * e] += bf16_lo(a[e]);
@@ -180,6 +180,7 @@ __global__ __launch_bounds__(kThreads) void kstats_kernel(const float* __restric
 }
 
 hipError_t launch_pool(int d, int64_t BH, int64_t N, int block, const void* k, const void* v,
+                       const Strides& kv,
                        float* kbar, float* vbar, uint16_t* kp, uint16_t* vbt, int64_t Mp,
                        hipStream_t stream) {
   const int64_t M = (N + block - 1) / block;
@@ -187,10 +188,12 @@ hipError_t launch_pool(int d, int64_t BH, int64_t N, int block, const void* k, c
   dim3 grid((unsigned)gx, (unsigned)BH);
   if (d == 64)
     hipLaunchKernelGGL(pool_kv_kernel<64>, grid, dim3(kThreads), 0, stream,
-                       (const uint16_t*)k, (const uint16_t*)v, N, block, M, Mp, kbar, vbar, kp, vbt);
+                       (const uint16_t*)k, (const uint16_t*)v, kv, N, block, M, Mp, kbar, vbar, kp,
+                       vbt);
   else
     hipLaunchKernelGGL(pool_kv_kernel<128>, grid, dim3(kThreads), 0, stream,
-                       (const uint16_t*)k, (const uint16_t*)v, N, block, M, Mp, kbar, vbar, kp, vbt);
+                       (const uint16_t*)k, (const uint16_t*)v, kv, N, block, M, Mp, kbar, vbar, kp,
+                       vbt);
   return hipGetLastError();
 }
 

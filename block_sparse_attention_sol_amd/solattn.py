@@ -32,6 +32,8 @@ EXPORTS = (
     "sol_select_topp",
     "sol_mfma_probe",
     "sol_dense_fwd",
+    "sol_attn_fwd_strided",
+    "sol_dense_fwd_strided",
     "sol_status_str",
     "sol_last_error",
     "sol_version",
@@ -41,6 +43,10 @@ EXPORTS = (
 class SolShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
                 ("d", ctypes.c_int64)]
+
+
+class SolStrides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("n", ctypes.c_int64)]
 
 
 class SolAttnDebug(ctypes.Structure):
@@ -80,12 +86,16 @@ def load_library(path: str = LIB_PATH):
                                     ctypes.POINTER(SolAttnDebug), vp]
     lib.sol_dense_fwd.argtypes = [shp, vp, vp, vp, vp, vp, vp]
     lib.sol_mfma_probe.argtypes = [ci, ci, vp, vp]
+    stp = ctypes.POINTER(SolStrides)
+    lib.sol_attn_fwd_strided.argtypes = [shp, stp, stp, vp, vp, vp, cf, ci, vp, vp, sz, vp]
+    lib.sol_dense_fwd_strided.argtypes = [shp, stp, stp, vp, vp, vp, vp, vp, vp]
     lib.sol_attn_fwd_masked.argtypes = [shp, vp, vp, vp, vp, ci, ci, vp, vp, sz, vp]
     lib.sol_proxy_map.argtypes = [shp, vp, vp, ci, vp, vp, sz, vp]
     lib.sol_select_topk.argtypes = [shp, ci, vp, ctypes.c_int64, vp, vp]
     lib.sol_select_topp.argtypes = [shp, ci, vp, cf, vp, vp]
     for f in ("sol_pool_kv", "sol_attn_fwd", "sol_attn_fwd_ex", "sol_dense_fwd", "sol_mfma_probe",
-              "sol_attn_fwd_masked", "sol_proxy_map", "sol_select_topk", "sol_select_topp"):
+              "sol_attn_fwd_masked", "sol_proxy_map", "sol_select_topk", "sol_select_topp",
+              "sol_attn_fwd_strided", "sol_dense_fwd_strided"):
         getattr(lib, f).restype = ci
     lib.sol_status_str.argtypes = [ci]
     lib.sol_status_str.restype = ctypes.c_char_p
@@ -108,15 +118,30 @@ def _shape(q) -> SolShape:
     return SolShape(B, H, N, d)
 
 
-def _dev(t, name):
-    import torch
+def _dev(t, name, strided: bool = False):
     if t is None:
         return None
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
-    if not t.is_contiguous():
+    if strided:
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError(f"{name} must be a [B, H, N, d] view with contiguous d")
+    elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _strides(t) -> SolStrides:
+    return SolStrides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _strided_call(q, k, v, out) -> bool:
+    """Whether the views need the strided entries (any non-contiguous tensor)."""
+    if all(t.is_contiguous() for t in (q, k, v, out)):
+        return False
+    if not (q.stride() == k.stride() == v.stride()):
+        raise ValueError("q, k and v must share one stride layout")
+    return True
 
 
 def _stream(stream):
@@ -172,6 +197,15 @@ def attn_fwd(q, k, v, beta: float, block: int, out=None, workspace=None, debug: 
     if workspace is None:
         workspace = new_workspace(q.shape, block, q.device)
     shp = _shape(q)
+    if _strided_call(q, k, v, out):
+        if debug or drop_unselected or events is not None:
+            raise ValueError("debug outputs, the drop ablation and events need contiguous tensors")
+        _check(lib.sol_attn_fwd_strided(ctypes.byref(shp), ctypes.byref(_strides(q)),
+                                        ctypes.byref(_strides(out)), _dev(q, "q", True),
+                                        _dev(k, "k", True), _dev(v, "v", True), float(beta), block,
+                                        _dev(out, "out", True), _dev(workspace, "workspace"),
+                                        workspace.numel(), _stream(stream)))
+        return out
     if not debug and not drop_unselected and events is None:
         _check(lib.sol_attn_fwd(ctypes.byref(shp), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
                                 float(beta), block, _dev(out, "out"), _dev(workspace, "workspace"),
@@ -212,6 +246,14 @@ def dense_fwd(q, k, v, out=None, want_lse: bool = False, stream=None):
     if out is None:
         out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if want_lse else None
+    if _strided_call(q, k, v, out):
+        _check(lib.sol_dense_fwd_strided(ctypes.byref(_shape(q)), ctypes.byref(_strides(q)),
+                                         ctypes.byref(_strides(out)), _dev(q, "q", True),
+                                         _dev(k, "k", True), _dev(v, "v", True),
+                                         _dev(out, "out", True),
+                                         _dev(lse, "lse") if lse is not None else None,
+                                         _stream(stream)))
+        return (out, lse) if want_lse else out
     _check(lib.sol_dense_fwd(ctypes.byref(_shape(q)), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
                              _dev(out, "out"), _dev(lse, "lse") if lse is not None else None,
                              _stream(stream)))

@@ -57,6 +57,16 @@ typedef struct sol_shape {
   int64_t B, H, N, d;
 } sol_shape;
 
+/* Element strides of a [B][H][N][d] view whose d elements are contiguous: element (b, h, n, c)
+ * is at ptr[b * b_stride + h * h_stride + n * n_stride + c].  The contiguous layout is
+ * {H*N*d, N*d, d}; a transformer's [B][N][H][d] projection output is {N*H*d, d, H*d}; q, k, v
+ * views into a packed [B][N][3][H][d] projection are {N*3*H*d, d, 3*H*d}.  Accepted strides are
+ * non-negative multiples of 8 with n_stride >= d (n_stride <= 2^23); an output view must not map
+ * two elements to one address. */
+typedef struct sol_strides {
+  int64_t b, h, n;
+} sol_strides;
+
 /* Query rows handled together by one tile of the fused kernel.  A key block is computed for a
  * tile when any row of the tile keeps it (rows that do not keep it are masked inside the tile). */
 #define SOL_QUERY_TILE 128
@@ -112,12 +122,28 @@ int sol_attn_fwd_ex(const sol_shape* shape, const void* q, const void* k, const 
                     const sol_attn_debug* dbg, void* stream);
 
 /*
+ * sol_attn_fwd on strided views (no transposes needed in a transformer block): q, k and v share
+ * in_strides, out uses out_strides (either NULL = contiguous).  The workspace is as for
+ * sol_attn_fwd.  SOL_EINVAL for strides outside the accepted set (see sol_strides) or an output
+ * view that overlaps an input or the workspace; otherwise as sol_attn_fwd.
+ */
+int sol_attn_fwd_strided(const sol_shape* shape, const sol_strides* in_strides,
+                         const sol_strides* out_strides, const void* q, const void* k,
+                         const void* v, float beta, int block, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
  * Dense reference attention: out = softmax(q k^T / sqrt(d)) v over all N keys, no mask.  The
  * speedup of the sparse pass is measured against this.
  *   q, k, v, out  [B][H][N][d] bf16, device.   lse  [B][H][N] fp32, device, or NULL.
  */
 int sol_dense_fwd(const sol_shape* shape, const void* q, const void* k, const void* v, void* out,
                   float* lse, void* stream);
+
+/* sol_dense_fwd on strided views (strides as for sol_attn_fwd_strided). */
+int sol_dense_fwd_strided(const sol_shape* shape, const sol_strides* in_strides,
+                          const sol_strides* out_strides, const void* q, const void* k,
+                          const void* v, void* out, float* lse, void* stream);
 
 /*
  * Prior-art routing, for comparison (page above, paragraph on routing: top-k keeps a fixed number

@@ -195,3 +195,26 @@ def test_selection_block_limit(lib):
     smap, mask = _ptrs(2)
     assert lib.sol_select_topk(ctypes.byref(s), 64, smap, 3, mask, None) == solattn.SOL_EUNSUPPORTED
     assert b"2048" in lib.sol_last_error()
+
+
+def test_strides_reject(lib):
+    s = _shape(B=1, H=2, N=1000, d=128)
+    q, k, v, out, ws = _ptrs(5)
+    need = lib.sol_attn_workspace_bytes(ctypes.byref(s), 128)
+
+    def call(ins, outs):
+        return lib.sol_attn_fwd_strided(ctypes.byref(s), ctypes.byref(ins) if ins else None,
+                                        ctypes.byref(outs) if outs else None, q, k, v, 0.5, 128, out,
+                                        ws, need, None)
+    bnhd = solattn.SolStrides(1000 * 2 * 128, 128, 2 * 128)
+    assert call(solattn.SolStrides(2 * 1000 * 128, 1000 * 128, 64), None) == solattn.SOL_EINVAL  # n < d
+    assert b"below d" in lib.sol_last_error()
+    assert call(solattn.SolStrides(2 * 1000 * 128, 1000 * 128, 132), None) == solattn.SOL_EINVAL  # not x8
+    assert call(None, solattn.SolStrides(0, 64, 256)) == solattn.SOL_EINVAL  # heads overlap rows
+    assert b"overlap" in lib.sol_last_error()
+    # valid layouts get past stride validation (and fail later on the workspace size check only)
+    st = lib.sol_attn_fwd_strided(ctypes.byref(s), ctypes.byref(bnhd), ctypes.byref(bnhd), q, k, v,
+                                  0.5, 128, out, ws, 16, None)
+    assert st == solattn.SOL_EWORKSPACE
+    assert lib.sol_dense_fwd_strided(ctypes.byref(s), ctypes.byref(bnhd), None, q, k, None, out, None,
+                                     None) == solattn.SOL_EINVAL
