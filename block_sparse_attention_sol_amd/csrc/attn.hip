@@ -65,30 +65,31 @@ __device__ __forceinline__ int tile_off(int row, int ch) {  // byte offset of a 
 
 // Copy rows [row0, row0 + ROWS) of a row-major [*, D] bf16 matrix into an LDS tile with
 // global_load_lds (16 bytes per lane, no registers).  Rows >= limit read row limit - 1 instead
-// (finite data; such keys are masked).  Every thread issues ROWS * D / 8 / kThreads loads.
-template <int D, int ROWS>
+// (finite data; such keys are masked).  Every thread of an NT-thread workgroup issues
+// ROWS * D / 8 / NT loads.
+template <int D, int ROWS, int NT = kThreads>
 __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ src, int64_t row0,
                                           int64_t limit, lds_u8* tile) {
   constexpr int kChunks = D / 8;
-  constexpr int kIters = ROWS * kChunks / kThreads;
-  static_assert(ROWS * kChunks % kThreads == 0, "tile must split into whole wave loads");
+  constexpr int kIters = ROWS * kChunks / NT;
+  static_assert(ROWS * kChunks % NT == 0, "tile must split into whole wave loads");
   const int t = threadIdx.x;
   const int wave = t >> 6;
 #pragma unroll
   for (int i = 0; i < kIters; ++i) {
-    const int p = i * kThreads + t;  // physical slot written by this lane
+    const int p = i * NT + t;  // physical slot written by this lane
     const int row = p / kChunks;
     const int ch = swz<D>(row, p % kChunks);  // logical chunk stored in that slot (XOR involution)
     int64_t grow = row0 + row;
     if (grow >= limit) grow = limit - 1;
     const uint16_t* g = src + grow * D + ch * 8;
-    lds_u8* dst = tile + (i * kThreads + wave * 64) * 16;  // wave-uniform; lane l lands at +16 l
+    lds_u8* dst = tile + (i * NT + wave * 64) * 16;  // wave-uniform; lane l lands at +16 l
     __builtin_amdgcn_global_load_lds((const void*)g, (__attribute__((address_space(3))) void*)dst,
                                      16, 0, 0);
   }
 }
-template <int D, int ROWS>
-constexpr int tile_loads() { return ROWS * (D / 8) / kThreads; }
+template <int D, int ROWS, int NT = kThreads>
+constexpr int tile_loads() { return ROWS * (D / 8) / NT; }
 
 // Buffer resource descriptor over `bytes` bytes at `base` (raw buffer: stride 0, 32-bit dword
 // data format): loads past `bytes` return zeros.  Built from wave-uniform values, so it lives in
@@ -107,14 +108,14 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
 // Per-lane byte offsets, within a ROWS-row tile of a bf16 matrix with rows of D contiguous
 // elements sn elements apart, of the 16 bytes each lane copies so that the LDS tile comes out
 // swizzled (see load_tile).
-template <int D, int ROWS>
+template <int D, int ROWS, int NT = kThreads>
 struct TileOffsets {
-  uint32_t v[tile_loads<D, ROWS>()];
+  uint32_t v[tile_loads<D, ROWS, NT>()];
   __device__ __forceinline__ explicit TileOffsets(int64_t sn) {
     constexpr int kChunks = D / 8;
 #pragma unroll
-    for (int i = 0; i < tile_loads<D, ROWS>(); ++i) {
-      const int p = i * kThreads + (int)threadIdx.x;
+    for (int i = 0; i < tile_loads<D, ROWS, NT>(); ++i) {
+      const int p = i * NT + (int)threadIdx.x;
       const int row = p / kChunks;
       v[i] = (uint32_t)(row * sn * 2 + swz<D>(row, p % kChunks) * 16);
     }
@@ -132,15 +133,15 @@ struct TileOffsets {
 // math.  The instruction has no register result (its destination is LDS), its address operands
 // are consumed at issue, and the callers order the LDS traffic themselves: wait_vmcnt before the
 // barrier that publishes a tile, and a barrier before a buffer is refilled.
-template <int D, int ROWS>
+template <int D, int ROWS, int NT = kThreads>
 __device__ __forceinline__ void load_tile_buf(i32x4_t rsrc, uint32_t soff,
-                                              const TileOffsets<D, ROWS>& off, lds_u8* tile) {
+                                              const TileOffsets<D, ROWS, NT>& off, lds_u8* tile) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-  for (int i = 0; i < tile_loads<D, ROWS>(); ++i) {
+  for (int i = 0; i < tile_loads<D, ROWS, NT>(); ++i) {
     // wave-uniform destination (lane l lands at +16 l); the LDS pointer itself is an operand, so
     // the compiler knows this statement writes there
-    lds_u8* dst = tile + (i * kThreads + wave * 64) * 16;
+    lds_u8* dst = tile + (i * NT + wave * 64) * 16;
     // m0 (the LDS destination base of the copy) is saved and restored around the copy
     uint32_t saved;
     __asm__ __volatile__(
@@ -164,12 +165,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Rows [r0, r0 + ROWS) of a row-strided bf16 matrix (row r at base + r * sn, rows below `limit`)
 // into an LDS tile; rows at or beyond `limit` read as zeros (the buffer ends after the last valid
 // row, and every later row starts at or beyond that end since sn >= D).
-template <int D, int ROWS>
+template <int D, int ROWS, int NT = kThreads>
 __device__ __forceinline__ void load_rows(const uint16_t* base, int64_t r0, int64_t limit, int64_t sn,
-                                          const TileOffsets<D, ROWS>& off, lds_u8* tile) {
+                                          const TileOffsets<D, ROWS, NT>& off, lds_u8* tile) {
   const int64_t n = limit - r0 < ROWS ? limit - r0 : ROWS;
   const uint32_t bytes = (uint32_t)((n - 1) * sn * 2 + D * 2);
-  load_tile_buf<D, ROWS>(make_rsrc(base + r0 * sn, bytes), 0u, off, tile);
+  load_tile_buf<D, ROWS, NT>(make_rsrc(base + r0 * sn, bytes), 0u, off, tile);
 }
 
 // Workgroup barrier without the memory fence of __syncthreads: the pipelined loops order their
@@ -266,20 +267,20 @@ __device__ __forceinline__ void pv32(const lds_u8* vtile, int kr0, const uint32_
 template <int D>
 __device__ __forceinline__ int vbt_off(int row, int ch) { return row * 64 + ((ch ^ ((row >> 2) & 3)) << 4); }
 
-template <int D>
+template <int D, int NT = kThreads>
 __device__ __forceinline__ void load_vbt_chunk(const uint16_t* __restrict__ vt, int64_t Mp, int cb,
                                                lds_u8* tile) {
-  constexpr int kIters = D * 4 / kThreads;
-  static_assert(D * 4 % kThreads == 0, "tile must split into whole wave loads");
+  constexpr int kIters = D * 4 / NT;
+  static_assert(D * 4 % NT == 0, "tile must split into whole wave loads");
   const int t = threadIdx.x;
   const int wave = t >> 6;
 #pragma unroll
   for (int i = 0; i < kIters; ++i) {
-    const int p = i * kThreads + t;
+    const int p = i * NT + t;
     const int row = p >> 2;
     const int ch = (p & 3) ^ ((row >> 2) & 3);
     const uint16_t* g = vt + (int64_t)row * Mp + (int64_t)cb * 32 + ch * 8;
-    lds_u8* dst = tile + (i * kThreads + wave * 64) * 16;
+    lds_u8* dst = tile + (i * NT + wave * 64) * 16;
     __builtin_amdgcn_global_load_lds((const void*)g, (__attribute__((address_space(3))) void*)dst,
                                      16, 0, 0);
   }
@@ -655,8 +656,14 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(RowStatsArgs a) {
 // Fused Sol-Attn kernel
 // ---------------------------------------------------------------------------------------------
 
-template <int D, int BLK>
-__global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
+// WAVES waves (32 query rows each) share each staged K/V tile: 4 (one 128-row tile, two
+// workgroups per CU) or 8 (two 128-row tiles, one workgroup per CU, every copy feeding twice the
+// rows; d = 128 only, whose 32-row pooled-key chunks split into whole loads for 512 threads).
+template <int D, int BLK, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void sol_attn_kernel(SparseArgs a) {
+  constexpr int NT = 64 * WAVES;       // threads
+  constexpr int QT = 32 * WAVES;       // query rows per workgroup
+  constexpr int HALVES = WAVES / 4;    // 128-row tiles per workgroup
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   lds_u8* smem = (lds_u8*)smem_raw;
   constexpr int kTileBytes = kStage * D * 2;          // one 64-row tile
@@ -665,17 +672,18 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
   constexpr int kRouteBuf = 4 * kChunkTile;           // Kbar lo, mid, hi + Vbar^T
   constexpr int kRegionA = 2 * kStageBytes > 2 * kRouteBuf ? 2 * kStageBytes : 2 * kRouteBuf;
   constexpr int kStagesPerBlock = BLK / kStage;
-  uint32_t* umask = (uint32_t*)(smem_raw + kRegionA);
+  uint32_t* umask = (uint32_t*)(smem_raw + kRegionA);  // [HALVES][W]: union of each 128-row tile
   const int W = (int)(a.Mp / 32);
 
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, c = lane & 31, h = lane >> 5;
-  const int64_t ntiles = (a.N + kQTile - 1) / kQTile;
+  const int64_t ntiles = (a.N + QT - 1) / QT;
   int64_t w;
   if (!work_item(a.BH * ntiles, w)) return;
   const int64_t bh = w / ntiles;
   const int64_t tile = w % ntiles;
-  const int64_t row0 = tile * kQTile + wave * 32;   // first row of this wave
+  const int64_t row0 = tile * QT + wave * 32;   // first row of this wave
+  uint32_t* my_umask = umask + (wave >> 2) * W;  // this wave's 128-row tile
   const int64_t row = row0 + c;
   const bool rvalid = row < a.N;
 
@@ -698,7 +706,7 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
   const float l2n_full = log2f((float)a.block);
   const float l2n_last = log2f((float)n_last);
 
-  for (int i = t; i < W; i += kThreads) umask[i] = 0u;
+  for (int i = t; i < HALVES * W; i += NT) umask[i] = 0u;
 
   // ---- pooled sweep: selection bits, tile union, pooled tokens ----
   // Chunks of 32 blocks, double buffered: chunk tiles 0..2 = lo, mid, hi pieces of Kbar,
@@ -714,10 +722,10 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
   const int nchunks = (int)(a.Mp / 32);
   auto issue_chunk = [&](int cb, int b) {
     lds_u8* base = smem + b * kRouteBuf;
-    load_tile<D, 32>(kp0 + 2 * piece, (int64_t)cb * 32, a.Mp, base);
-    load_tile<D, 32>(kp0 + 1 * piece, (int64_t)cb * 32, a.Mp, base + kChunkTile);
-    load_tile<D, 32>(kp0, (int64_t)cb * 32, a.Mp, base + 2 * kChunkTile);
-    load_vbt_chunk<D>(vt0, a.Mp, cb, base + 3 * kChunkTile);
+    load_tile<D, 32, NT>(kp0 + 2 * piece, (int64_t)cb * 32, a.Mp, base);
+    load_tile<D, 32, NT>(kp0 + 1 * piece, (int64_t)cb * 32, a.Mp, base + kChunkTile);
+    load_tile<D, 32, NT>(kp0, (int64_t)cb * 32, a.Mp, base + 2 * kChunkTile);
+    load_vbt_chunk<D, NT>(vt0, a.Mp, cb, base + 3 * kChunkTile);
   };
   // the caller's selection word of this row for chunk cb (loaded one chunk ahead, with the copy)
   const uint32_t* min_row = a.mask_in ? a.mask_in + (bh * a.N + row) * W : nullptr;
@@ -768,7 +776,7 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
       if (a.mask_out) a.mask_out[(bh * a.N + row) * W + cb] = word;
     }
     // tile union: one LDS atomic OR per row (no dependent cross-lane reduction)
-    if (h == 0 && word) atomicOr(&umask[cb], word);
+    if (h == 0 && word) atomicOr(&my_umask[cb], word);
     if (!a.drop) {
       cmax = pair_max(cmax);
       const bool grow = cmax > mrun + kSlack;
@@ -808,7 +816,10 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
       }
       while (it_u == 0u) {
         if (++it_w >= W) return false;
-        it_u = __builtin_amdgcn_readfirstlane(umask[it_w]);
+        uint32_t u = umask[it_w];
+#pragma unroll
+        for (int hh = 1; hh < HALVES; ++hh) u |= umask[hh * W + it_w];
+        it_u = __builtin_amdgcn_readfirstlane(u);
       }
       const int b = __builtin_ctz(it_u);
       it_u &= it_u - 1u;
@@ -816,12 +827,12 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
       it_s = -1;
     }
   };
-  const TileOffsets<D, kStage> toff(sn);
+  const TileOffsets<D, kStage, NT> toff(sn);
   auto issue = [&](int j, int s, int buf) {
     const int64_t r0 = (int64_t)j * BLK + s * kStage;
     lds_u8* base = smem + buf * kStageBytes;
-    load_rows<D, kStage>(kb, r0, a.N, sn, toff, base);
-    load_rows<D, kStage>(vb, r0, a.N, sn, toff, base + kTileBytes);
+    load_rows<D, kStage, NT>(kb, r0, a.N, sn, toff, base);
+    load_rows<D, kStage, NT>(vb, r0, a.N, sn, toff, base + kTileBytes);
   };
 
   // One barrier per stage: it publishes the stage's copy (each lane waited for its own loads)
@@ -831,7 +842,6 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
   auto load_word = [&](int wd) -> uint32_t {
     return rvalid ? rmask[(int64_t)wd * a.N + row] : 0u;
   };
-  int kept_blocks = 0;
   int cur_j = -1, cur_s = 0;
   bool have = next_stage(cur_j, cur_s);
   int mask_w = -1;
@@ -856,7 +866,6 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
         next_word = load_word(next_w);
       }
     }
-    if (cur_s == 0) ++kept_blocks;
     const bool active = (mask_word >> (cur_j & 31)) & 1u;
     const int r0 = cur_j * BLK + cur_s * kStage;
     const int nvalid = (int)a.N - r0 < kStage ? (int)a.N - r0 : kStage;
@@ -872,7 +881,13 @@ __global__ __launch_bounds__(kThreads, 2) void sol_attn_kernel(SparseArgs a) {
     mask_word = next_word;
     have = more;
   }
-  if (a.tile_kept && t == 0) a.tile_kept[bh * ntiles + tile] = kept_blocks;
+  if (a.tile_kept && t < HALVES) {  // blocks kept by some row of each 128-row tile
+    const int64_t nt128 = (a.N + kQTile - 1) / kQTile;
+    const int64_t t128 = tile * HALVES + t;
+    int kept = 0;
+    for (int i = 0; i < W; ++i) kept += __builtin_popcount(umask[t * W + i]);
+    if (t128 < nt128) a.tile_kept[bh * nt128 + t128] = kept;
+  }
   bar();  // every wave is done with the stage buffers before the epilogue reuses them
 
   epilogue<D>(o, mrun, lsum, row0, a.N, a.out + a.outs.base(bh), a.outs.sn,
@@ -1087,11 +1102,11 @@ __global__ __launch_bounds__(kThreads, 2) void dense_attn_kernel(const uint16_t*
 // Launchers
 // ---------------------------------------------------------------------------------------------
 
-static size_t sparse_smem_bytes(int d, int64_t Mp) {
+static size_t sparse_smem_bytes(int d, int64_t Mp, int halves) {
   const size_t stage = (size_t)2 * kStage * d * 2;
   const size_t route = (size_t)4 * 32 * d * 2;
   const size_t regionA = 2 * stage > 2 * route ? 2 * stage : 2 * route;
-  return regionA + (size_t)(Mp / 32) * 4;
+  return regionA + (size_t)halves * (Mp / 32) * 4;
 }
 
 template <typename K>
@@ -1102,22 +1117,25 @@ static hipError_t set_smem(K kern, size_t bytes) {
 
 static unsigned xcd_grid(int64_t total) { return (unsigned)(((total + 7) / 8) * 8); }
 
-template <int D, int BLK>
+template <int D, int BLK, int WAVES>
 static hipError_t launch_sparse_t(const SparseArgs& a, hipStream_t stream) {
-  const size_t smem = sparse_smem_bytes(D, a.Mp);
-  auto kern = sol_attn_kernel<D, BLK>;
+  const size_t smem = sparse_smem_bytes(D, a.Mp, WAVES / 4);
+  auto kern = sol_attn_kernel<D, BLK, WAVES>;
   hipError_t err = set_smem(kern, smem);
   if (err != hipSuccess) return err;
-  const int64_t ntiles = (a.N + kQTile - 1) / kQTile;
-  hipLaunchKernelGGL(kern, dim3(xcd_grid(a.BH * ntiles)), dim3(kThreads), smem, stream, a);
+  const int64_t ntiles = (a.N + 32 * WAVES - 1) / (32 * WAVES);
+  hipLaunchKernelGGL(kern, dim3(xcd_grid(a.BH * ntiles)), dim3(64 * WAVES), smem, stream, a);
   return hipGetLastError();
 }
 
+// Four waves per workgroup and two workgroups per CU: measured at the Wan2.1-14B shape, eight
+// waves (one workgroup per CU, each copy shared by twice the rows) were 9% slower -- the second
+// workgroup's independent progress is worth more than the halved copy traffic.
 hipError_t launch_sparse(int d, const SparseArgs& a, hipStream_t stream) {
-  if (d == 64 && a.block == 64) return launch_sparse_t<64, 64>(a, stream);
-  if (d == 64 && a.block == 128) return launch_sparse_t<64, 128>(a, stream);
-  if (d == 128 && a.block == 64) return launch_sparse_t<128, 64>(a, stream);
-  return launch_sparse_t<128, 128>(a, stream);
+  if (d == 64 && a.block == 64) return launch_sparse_t<64, 64, 4>(a, stream);
+  if (d == 64 && a.block == 128) return launch_sparse_t<64, 128, 4>(a, stream);
+  if (d == 128 && a.block == 64) return launch_sparse_t<128, 64, 4>(a, stream);
+  return launch_sparse_t<128, 128, 4>(a, stream);
 }
 
 template <int D>
