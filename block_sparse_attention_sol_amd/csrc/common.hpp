@@ -91,18 +91,4 @@ __device__ __forceinline__ uint32_t pair_or(uint32_t x) {
   return a | b;
 }
 
-// LDS row-major tile with rows of `kChunks` 16-byte chunks; chunk index XOR-swizzled by the row so
-// that 8 consecutive rows read at the same logical chunk hit 8 distinct bank groups.
-template <int kChunks>
-__device__ __forceinline__ int swz16(int row, int chunk) {
-  return row * kChunks + (chunk ^ (row & 7));
-}
-
-// Transposed V tile in LDS: Vt[d][key], rows of kSlots 8-byte slots (4 bf16 keys each), slot index
-// XOR-swizzled by the row so 16 consecutive d rows reading one logical slot are conflict-free.
-template <int kSlots>
-__device__ __forceinline__ int swz8(int row, int slot) {
-  return row * kSlots + (slot ^ (row & 15));
-}
-
 }  // namespace solattn
