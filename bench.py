@@ -486,7 +486,7 @@ def main():
             "traffic": recorded_traffic(
                 [os.path.join(ROOT, "block_sparse_attention_sol_amd", "csrc", f)
                  for f in ("attn.hip", "common.hpp", "kernels.hpp")], w.name, beta),
-            "kernel": "sol_attn_kernel<128,128> (fused routing + pooled tokens + exact attention)",
+            "kernel": "sol_attn_kernel<128,128,4> (fused routing + pooled tokens + exact attention)",
             "flops": "kept-block FLOPs F_tile: 4*d per (row, key) of each block some row of the "
                      "row's 128-row query tile keeps",
         },

@@ -164,12 +164,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Rows [r0, r0 + ROWS) of a row-strided bf16 matrix (row r at base + r * sn, rows below `limit`)
 // into an LDS tile; rows at or beyond `limit` read as zeros (the buffer ends after the last valid
-// row, and every later row starts at or beyond that end since sn >= D).
+// row, and every later row starts at or beyond that end since sn >= D).  The buffer covers all
+// the remaining valid rows, not just this tile's: measured on gfx950, a resource cut to the tile
+// made the dense loop fetch 3.7x more bytes from beyond L2.
 template <int D, int ROWS, int NT = kThreads>
 __device__ __forceinline__ void load_rows(const uint16_t* base, int64_t r0, int64_t limit, int64_t sn,
                                           const TileOffsets<D, ROWS, NT>& off, lds_u8* tile) {
-  const int64_t n = limit - r0 < ROWS ? limit - r0 : ROWS;
-  const uint32_t bytes = (uint32_t)((n - 1) * sn * 2 + D * 2);
+  const int64_t rest = (limit - r0 - 1) * sn * 2 + D * 2;
+  const uint32_t bytes = (uint32_t)(rest < 0xffffffffll ? rest : 0xffffffffll);
   load_tile_buf<D, ROWS, NT>(make_rsrc(base + r0 * sn, bytes), 0u, off, tile);
 }
 
