@@ -387,8 +387,11 @@ def main():
     kept_blocks = int(dbg["tile_kept"].sum().item())
     rho_tile = kept_blocks / (B * H * T * M)
     F_tile = sol.kept_block_flops(dbg["tile_kept"], dbg["mask"], N, d, w.block)
-    units = sol.union_units(dbg["mask"], N, w.block)
-    F_row, F_exec = 4.0 * d * units[1], 4.0 * d * units[32]
+    # the fused kernel skips a key block per wave when none of the wave's rows keeps it: waves of
+    # 16 rows at head dimension 128, of 32 rows at 64
+    wave_rows = 16 if d == 128 else 32
+    units = sol.union_units(dbg["mask"], N, w.block, heights=(1, wave_rows, sol.QUERY_TILE))
+    F_row, F_exec = 4.0 * d * units[1], 4.0 * d * units[wave_rows]
     mask = dbg["mask"].view(torch.int32)
     row_bits = sum(int(torch.bitwise_and(torch.bitwise_right_shift(mask, s), 1).sum().item())
                    for s in range(32))
@@ -434,7 +437,7 @@ def main():
     dense_F = sol.dense_flops(B, H, N, d)
     pool_bytes = 2 * B * H * N * d * 2 + 2 * B * H * M * d * 4  # K,V read + Kbar,Vbar (fp32) written
     # algorithmic work: 4*d FLOPs per (row, key) of every kept (128-row tile, block) pair; the
-    # matrix cores skip, per 32-row wave, blocks none of its rows keeps, so they execute F_exec
+    # matrix cores skip, per wave, blocks none of its rows keeps, so they execute F_exec
     achieved = F_tile / (t_fused * 1e-3) / 1e12
     executed = F_exec / (t_fused * 1e-3) / 1e12
     result = {
@@ -486,7 +489,8 @@ def main():
             "traffic": recorded_traffic(
                 [os.path.join(ROOT, "block_sparse_attention_sol_amd", "csrc", f)
                  for f in ("attn.hip", "common.hpp", "kernels.hpp")], w.name, beta),
-            "kernel": "sol_attn_kernel<128,128,4> (fused routing + pooled tokens + exact attention)",
+            "kernel": ("sol_attn16_kernel<128,128>" if d == 128 else "sol_attn_kernel<64,64,4>")
+                      + " (fused routing + pooled tokens + exact attention)",
             "flops": "kept-block FLOPs F_tile: 4*d per (row, key) of each block some row of the "
                      "row's 128-row query tile keeps",
         },

@@ -48,14 +48,16 @@ constexpr int kRowStatsTiles = 16;  // query tiles per row-statistics workgroup 
 
 // ---------------------------------------------------------------------------------------------
 // LDS tiles: row-major [rows][D] bf16, 16-byte chunks XOR-swizzled per row.  The swizzle makes
-// both access patterns conflict-free on a 256-byte-wide LDS: 16 consecutive rows read at one
+// the access patterns conflict-free on a 256-byte-wide LDS: 16 consecutive rows read at one
 // logical chunk (the K / Kbar A operand) land on 16 distinct 16-byte bank groups, and the
-// transpose read of V -- 4 consecutive rows x 4 adjacent chunks per 32 lanes -- lands each row
-// in its own 64-byte quarter.
+// transpose reads of V land on distinct chunks per 32 lanes -- 4 consecutive rows x 4 adjacent
+// chunks (32x32 layout), or two 4-row groups x 2 chunks (16x16 layout, where bit 2 of the row
+// goes to chunk bit 1 so that the two groups differ in a bit the read does not cover).
 // ---------------------------------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ int swz(int row, int ch) {
-  if constexpr (D == 128) return ch ^ (((row & 3) << 2) | ((row >> 2) & 3));
+  if constexpr (D == 128)
+    return ch ^ (((row & 3) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1));
   else return ch ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
 template <int D>
@@ -111,11 +113,11 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
 template <int D, int ROWS, int NT = kThreads>
 struct TileOffsets {
   uint32_t v[tile_loads<D, ROWS, NT>()];
-  __device__ __forceinline__ explicit TileOffsets(int64_t sn) {
+  __device__ __forceinline__ explicit TileOffsets(int64_t sn, int tid = (int)threadIdx.x) {
     constexpr int kChunks = D / 8;
 #pragma unroll
     for (int i = 0; i < tile_loads<D, ROWS, NT>(); ++i) {
-      const int p = i * NT + (int)threadIdx.x;
+      const int p = i * NT + tid;
       const int row = p / kChunks;
       v[i] = (uint32_t)(row * sn * 2 + swz<D>(row, p % kChunks) * 16);
     }
@@ -133,26 +135,39 @@ struct TileOffsets {
 // math.  The instruction has no register result (its destination is LDS), its address operands
 // are consumed at issue, and the callers order the LDS traffic themselves: wait_vmcnt before the
 // barrier that publishes a tile, and a barrier before a buffer is refilled.
+// One copy of 16 bytes per lane from the buffer `rsrc` (at byte voff + soff) to LDS; lane l lands
+// at dst + 16 l, dst wave-uniform.  The LDS pointer itself is an operand, so the compiler knows
+// this statement writes there; m0 (the LDS destination base of the copy) is saved and restored
+// around it.
+__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t soff, lds_u8* dst) {
+  uint32_t saved;
+  __asm__ __volatile__(
+      "s_mov_b32 %[saved], m0\n\t"
+      "s_mov_b32 m0, %[m0]\n\t"
+      "buffer_load_dwordx4 %[voff], %[rsrc], %[soff] offen lds\n\t"
+      "s_mov_b32 m0, %[saved]"
+      : [saved] "=&s"(saved)
+      : [m0] "s"(dst), [voff] "v"(voff), [rsrc] "s"(rsrc), [soff] "s"(soff)
+      : "memory");
+}
+
 template <int D, int ROWS, int NT = kThreads>
 __device__ __forceinline__ void load_tile_buf(i32x4_t rsrc, uint32_t soff,
                                               const TileOffsets<D, ROWS, NT>& off, lds_u8* tile) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-  for (int i = 0; i < tile_loads<D, ROWS, NT>(); ++i) {
-    // wave-uniform destination (lane l lands at +16 l); the LDS pointer itself is an operand, so
-    // the compiler knows this statement writes there
-    lds_u8* dst = tile + (i * NT + wave * 64) * 16;
-    // m0 (the LDS destination base of the copy) is saved and restored around the copy
-    uint32_t saved;
-    __asm__ __volatile__(
-        "s_mov_b32 %[saved], m0\n\t"
-        "s_mov_b32 m0, %[m0]\n\t"
-        "buffer_load_dwordx4 %[voff], %[rsrc], %[soff] offen lds\n\t"
-        "s_mov_b32 m0, %[saved]"
-        : [saved] "=&s"(saved)
-        : [m0] "s"(dst), [voff] "v"(off.v[i]), [rsrc] "s"(rsrc), [soff] "s"(soff)
-        : "memory");
-  }
+  for (int i = 0; i < tile_loads<D, ROWS, NT>(); ++i)
+    dma16(rsrc, off.v[i], soff, tile + (i * NT + wave * 64) * 16);
+}
+
+// Rows [row0, row0 + ROWS) of a row-major [*, D] bf16 matrix whose rows all exist (pooled-key
+// pieces, padded to Mp rows), copied as load_tile does but without the compiler's LDS-DMA builtin
+// (see load_tile_buf): a builtin copy in flight makes the compiler wait for every outstanding
+// memory operation before the next LDS write, which stalls the routing sweep once per chunk.
+template <int D, int ROWS, int NT = kThreads>
+__device__ __forceinline__ void load_dense_rows(const uint16_t* src, int64_t row0,
+                                                const TileOffsets<D, ROWS, NT>& off, lds_u8* tile) {
+  load_tile_buf<D, ROWS, NT>(make_rsrc(src + row0 * D, ROWS * D * 2), 0u, off, tile);
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -265,27 +280,36 @@ __device__ __forceinline__ void pv32(const lds_u8* vtile, int kr0, const uint32_
 
 // Vbar^T chunk tile: D rows (head dimension) x 32 blocks, 64-byte rows of four 16-byte chunks,
 // chunk index XOR (row / 4) % 4 so that 16 consecutive rows read at one position are spread over
-// the banks.  Copied with global_load_lds from vbt [D][Mp] (block index contiguous).
+// the banks.  Copied from vbt [D][Mp] (block index contiguous).
 template <int D>
 __device__ __forceinline__ int vbt_off(int row, int ch) { return row * 64 + ((ch ^ ((row >> 2) & 3)) << 4); }
 
+// Per-lane byte offsets of the Vbar^T chunk copy (relative to the chunk's first column): lane
+// slot p of the tile holds row p / 4, logical chunk (p % 4) XOR the row's swizzle.
 template <int D, int NT = kThreads>
-__device__ __forceinline__ void load_vbt_chunk(const uint16_t* __restrict__ vt, int64_t Mp, int cb,
-                                               lds_u8* tile) {
-  constexpr int kIters = D * 4 / NT;
+struct VbtOffsets {
   static_assert(D * 4 % NT == 0, "tile must split into whole wave loads");
-  const int t = threadIdx.x;
-  const int wave = t >> 6;
+  uint32_t v[D * 4 / NT];
+  __device__ __forceinline__ explicit VbtOffsets(int64_t Mp) {
 #pragma unroll
-  for (int i = 0; i < kIters; ++i) {
-    const int p = i * NT + t;
-    const int row = p >> 2;
-    const int ch = (p & 3) ^ ((row >> 2) & 3);
-    const uint16_t* g = vt + (int64_t)row * Mp + (int64_t)cb * 32 + ch * 8;
-    lds_u8* dst = tile + (i * NT + wave * 64) * 16;
-    __builtin_amdgcn_global_load_lds((const void*)g, (__attribute__((address_space(3))) void*)dst,
-                                     16, 0, 0);
+    for (int i = 0; i < D * 4 / NT; ++i) {
+      const int p = i * NT + (int)threadIdx.x;
+      const int row = p >> 2;
+      const int ch = (p & 3) ^ ((row >> 2) & 3);
+      v[i] = (uint32_t)(((int64_t)row * Mp + ch * 8) * 2);
+    }
   }
+};
+
+// The Vbar^T tile of chunk cb (blocks 32 cb .. 32 cb + 31) into LDS, with buffer loads issued from
+// asm (see load_dense_rows for why).
+template <int D, int NT = kThreads>
+__device__ __forceinline__ void load_vbt_buf(const uint16_t* vt, int64_t Mp, int cb,
+                                             const VbtOffsets<D, NT>& off, lds_u8* tile) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const i32x4_t rsrc = make_rsrc(vt + (int64_t)cb * 32, (uint32_t)(((D - 1) * Mp + 32) * 2));
+#pragma unroll
+  for (int i = 0; i < D * 4 / NT; ++i) dma16(rsrc, off.v[i], 0u, tile + (i * NT + wave * 64) * 16);
 }
 
 // O^T[ds] += Vbar^T P^T for the 32 pooled blocks of a chunk (probability registers as in pv32).
@@ -722,12 +746,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void sol_attn_kernel(SparseA
   float mrun = -1e30f;  // running max, log2 domain
   float lsum = 0.f;
   const int nchunks = (int)(a.Mp / 32);
+  const TileOffsets<D, 32, NT> coff(D);
+  const VbtOffsets<D, NT> voff(a.Mp);
   auto issue_chunk = [&](int cb, int b) {
     lds_u8* base = smem + b * kRouteBuf;
-    load_tile<D, 32, NT>(kp0 + 2 * piece, (int64_t)cb * 32, a.Mp, base);
-    load_tile<D, 32, NT>(kp0 + 1 * piece, (int64_t)cb * 32, a.Mp, base + kChunkTile);
-    load_tile<D, 32, NT>(kp0, (int64_t)cb * 32, a.Mp, base + 2 * kChunkTile);
-    load_vbt_chunk<D, NT>(vt0, a.Mp, cb, base + 3 * kChunkTile);
+    load_dense_rows<D, 32, NT>(kp0 + 2 * piece, (int64_t)cb * 32, coff, base);
+    load_dense_rows<D, 32, NT>(kp0 + 1 * piece, (int64_t)cb * 32, coff, base + kChunkTile);
+    load_dense_rows<D, 32, NT>(kp0, (int64_t)cb * 32, coff, base + 2 * kChunkTile);
+    load_vbt_buf<D, NT>(vt0, a.Mp, cb, voff, base + 3 * kChunkTile);
   };
   // the caller's selection word of this row for chunk cb (loaded one chunk ahead, with the copy)
   const uint32_t* min_row = a.mask_in ? a.mask_in + (bh * a.N + row) * W : nullptr;
@@ -897,6 +923,450 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void sol_attn_kernel(SparseA
               smem + wave * 32 * D * 2);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Fused kernel with 16-row waves (head dimension 128).  A 128-row query tile is split over eight
+// waves of 16 rows, on the 16x16x32 matrix instructions (lane row g = lane / 16 holds keys or
+// blocks 4g .. 4g + 3 of every 16, lane q = lane % 16 is the query).  Against the 4-wave kernel:
+//   * a wave skips a stage when none of its 16 rows keeps the block, so the math executed follows
+//     the kept blocks at 16-row rather than 32-row granularity;
+//   * two workgroups per CU give four waves per SIMD instead of two, to cover the latency of the
+//     waves that do have work.
+// The stage structure (routing sweep over 32-block chunks, then the tile union's 64-key stages,
+// double buffered, one barrier per stage) is that of sol_attn_kernel.
+// ---------------------------------------------------------------------------------------------
+constexpr int kWaves16 = 8;
+constexpr int kThreads16 = 64 * kWaves16;
+
+// The lane index, opaque to the optimiser: LDS addresses derived from it inside a loop are
+// recomputed each iteration (a few VALU operations) instead of being hoisted out and held in
+// registers for the whole loop, which at four waves per SIMD (128 VGPRs) would spill.
+__device__ __forceinline__ int fresh_lane() {
+  int l = threadIdx.x & 63;
+  __asm__ __volatile__("" : "+v"(l));
+  return l;
+}
+
+// Q fragments of this lane's query row for the 16x16x32 S^T products.  Lane row g takes the
+// head-dimension chunks kk + (D/32) g (d = 8 kk + (D/4) g ..) at step kk: the K reads of one step
+// then hit chunks D/32 apart across the lane rows, which the LDS serves without bank conflicts
+// (adjacent chunks per lane row, the other choice, run at half rate).
+template <int D>
+__device__ __forceinline__ void load_q16(const uint16_t* __restrict__ qrow, bool valid,
+                                         bf16x8 (&qf)[D / 32]) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (valid) raw = *reinterpret_cast<const u32x4*>(qrow + 8 * (kk + (D / 32) * g));
+    qf[kk] = __builtin_bit_cast(bf16x8, raw);
+  }
+}
+
+// S^T of the 16 rows kr0 .. kr0 + 15 of a swizzled LDS tile against this lane's query.
+template <int D>
+__device__ __forceinline__ f32x4 scores16(const lds_u8* tile, int kr0, const bf16x8 (&qf)[D / 32],
+                                          f32x4 acc, int lane) {
+  const int q = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const u32x4 raw = lds_read16(tile + tile_off<D>(kr0 + q, kk + (D / 32) * g));
+    acc = mfma16(__builtin_bit_cast(bf16x8, raw), qf[kk], acc);
+  }
+  return acc;
+}
+
+// Probabilities of one 32-key group as the B operand of O^T += V^T P^T: lane row g holds the
+// keys 4g .. 4g + 3 (from the first 16-key score tile) and 16 + 4g .. 16 + 4g + 3 (second tile),
+// which fixes the k order the A operand must follow.
+__device__ __forceinline__ bf16x8 p_operand16(const uint32_t (&pk)[4]) {
+  u32x4 w;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) w[m] = pk[m];
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// O^T[dt] += V^T P^T for one 32-key group (tile rows kr0 .. kr0 + 31 of a V tile).  The A operand
+// of lane (g, q) is V^T[16 dt + q][keys 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3 of the group]:
+// two LDS transpose reads, in which the 16 lanes of row g point at the four key rows (lane / 4)
+// and four column quads (lane % 4) and lane q receives column q of those rows.
+template <int D>
+__device__ __forceinline__ void pv16(const lds_u8* vtile, int kr0, const bf16x8& b,
+                                     f32x4 (&o)[D / 16], int lane) {
+  const int j = lane & 15, g = lane >> 4;
+  const int r1 = kr0 + 4 * g + (j >> 2), r2 = r1 + 16;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const int c = 16 * dt + 4 * (j & 3);
+    const int half = ((c >> 2) & 1) * 8;
+    const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(vtile + tile_off<D>(r1, c >> 3) + half));
+    const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(vtile + tile_off<D>(r2, c >> 3) + half));
+    u32x4 raw;
+    raw[0] = __builtin_bit_cast(u32x2, x0)[0];
+    raw[1] = __builtin_bit_cast(u32x2, x0)[1];
+    raw[2] = __builtin_bit_cast(u32x2, x1)[0];
+    raw[3] = __builtin_bit_cast(u32x2, x1)[1];
+    o[dt] = mfma16(__builtin_bit_cast(bf16x8, raw), b, o[dt]);
+  }
+}
+
+// O^T[dt] += Vbar^T P^T for the 32 pooled blocks of a routing chunk: the A operand of lane (g, q)
+// is row 16 dt + q of the Vbar^T chunk tile at blocks 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3,
+// two 8-byte reads.
+template <int D>
+__device__ __forceinline__ void pv_pooled16(const lds_u8* vt, const bf16x8& b, f32x4 (&o)[D / 16],
+                                            int lane) {
+  const int q = lane & 15, g = lane >> 4;
+  const int off = 8 * (g & 1);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const int row = 16 * dt + q;
+    const u32x2 x0 = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
+        vt + vbt_off<D>(row, g >> 1) + off);
+    const u32x2 x1 = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
+        vt + vbt_off<D>(row, 2 + (g >> 1)) + off);
+    u32x4 raw;
+    raw[0] = x0[0]; raw[1] = x0[1]; raw[2] = x1[0]; raw[3] = x1[1];
+    o[dt] = mfma16(__builtin_bit_cast(bf16x8, raw), b, o[dt]);
+  }
+}
+
+// Scale the running state by 2^(mrun - mt) when a taking-part row's new maximum mt exceeds the
+// running one by more than kSlack (wave-uniform branch; see kSlack).
+template <int D>
+__device__ __forceinline__ void raise_max16(float mt, bool active, float& mrun, float& lsum,
+                                            f32x4 (&o)[D / 16]) {
+  const bool grow = active && mt > mrun + kSlack;
+  if (__builtin_amdgcn_ballot_w64(grow)) {
+    const float mnew = grow ? mt : mrun;
+    const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+    mrun = mnew;
+    lsum *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[dt][i] *= alpha;
+  }
+}
+
+// One 64-key stage folded into this lane's running softmax (as exact_stage, 16-row layout).
+// Every lane of a query row holds the same running max; lsum is this lane's share of the row's
+// denominator (the four lane rows are added in the epilogue).
+template <int D>
+__device__ __forceinline__ void exact_stage16(const lds_u8* ktile, const lds_u8* vtile,
+                                              const bf16x8 (&qf)[D / 32], bool active, int nvalid,
+                                              float sl2, float& mrun, float& lsum,
+                                              f32x4 (&o)[D / 16], int lane) {
+  constexpr int NT16 = kStage / 16;  // 16-key score tiles per stage
+  const int g = lane >> 4;
+  f32x4 s[NT16];
+  // scheduling fences between tiles keep at most one tile's operand reads in flight (register
+  // budget of four waves per SIMD)
+#pragma unroll
+  for (int kt = 0; kt < NT16; ++kt) {
+    s[kt] = scores16<D>(ktile, 16 * kt, qf, f32x4{0.f, 0.f, 0.f, 0.f}, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (nvalid < kStage) {  // wave-uniform
+#pragma unroll
+    for (int kt = 0; kt < NT16; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (16 * kt + 4 * g + i >= nvalid) s[kt][i] = -INFINITY;
+  }
+  float mt = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < NT16; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[kt][i]);
+  mt = quad_max(mt) * sl2;
+  raise_max16<D>(mt, active, mrun, lsum, o);
+  // rows that do not take part subtract +inf: every probability is 0
+  const float moff = active ? -mrun : -INFINITY;
+  float ps = 0.f;
+#pragma unroll
+  for (int grp = 0; grp < NT16 / 2; ++grp) {
+    uint32_t pk[4];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const f32x4& sv = s[2 * grp + h2];
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[0], sl2, moff));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[1], sl2, moff));
+      const float p2 = __builtin_amdgcn_exp2f(fmaf(sv[2], sl2, moff));
+      const float p3 = __builtin_amdgcn_exp2f(fmaf(sv[3], sl2, moff));
+      pk[2 * h2] = pack_bf16x2(p0, p1);
+      pk[2 * h2 + 1] = pack_bf16x2(p2, p3);
+      ps = add_bf16x2(pk[2 * h2], ps);
+      ps = add_bf16x2(pk[2 * h2 + 1], ps);
+    }
+    pv16<D>(vtile, 32 * grp, p_operand16(pk), o, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  lsum += ps;
+}
+
+// Write O = O^T / l for the wave's 16 rows through LDS (row-major, swizzled) so that every global
+// store writes whole rows; also the optional fp32 output and log-sum-exp.
+template <int D>
+__device__ __forceinline__ void epilogue16(const f32x4 (&o)[D / 16], float mrun, float lsum,
+                                           int64_t row0, int64_t N, uint16_t* __restrict__ out,
+                                           int64_t on, float* __restrict__ out_f32,
+                                           float* __restrict__ lse, lds_u8* stage) {
+  const int lane = threadIdx.x & 63;
+  const int q = lane & 15, g = lane >> 4;
+  const int64_t row = row0 + q;
+  const float l = quad_sum(lsum);
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const float x0 = o[dt][0] * inv, x1 = o[dt][1] * inv, x2 = o[dt][2] * inv, x3 = o[dt][3] * inv;
+    u32x2 w;
+    w[0] = pack_bf16x2(x0, x1);
+    w[1] = pack_bf16x2(x2, x3);
+    // d = 16 dt + 4 g + (0..3): chunk 2 dt + g / 2, half g % 2
+    *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+        stage + tile_off<D>(q, 2 * dt + (g >> 1)) + 8 * (g & 1)) = w;
+    if (out_f32 && row < N)
+      *reinterpret_cast<f32x4*>(out_f32 + row * D + 16 * dt + 4 * g) = f32x4{x0, x1, x2, x3};
+  }
+  if (lse && g == 0 && row < N) lse[row] = l > 0.f ? (mrun + log2f(l)) * kLn2 : -INFINITY;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  constexpr int kChunks = D / 8;
+#pragma unroll
+  for (int i = 0; i < 16 * kChunks / 64; ++i) {
+    const int idx = i * 64 + lane;
+    const int r = idx / kChunks, ch = idx % kChunks;
+    const u32x4 v = lds_read16(stage + tile_off<D>(r, ch));
+    if (row0 + r < N) *reinterpret_cast<u32x4*>(out + (row0 + r) * on + ch * 8) = v;
+  }
+}
+
+template <int D, int BLK>
+__global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a) {
+  static_assert(D == 128, "the 16-row kernel serves head dimension 128");
+  constexpr int NT = kThreads16;
+  constexpr int QT = kQTile;                          // 128 query rows, 16 per wave
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  lds_u8* smem = (lds_u8*)smem_raw;
+  constexpr int kTileBytes = kStage * D * 2;          // one 64-row tile
+  constexpr int kStageBytes = 2 * kTileBytes;         // K + V
+  constexpr int kChunkTile = 32 * D * 2;              // one 32-row pooled tile
+  constexpr int kRouteBuf = 4 * kChunkTile;           // Kbar lo, mid, hi + Vbar^T
+  constexpr int kRegionA = 2 * kStageBytes > 2 * kRouteBuf ? 2 * kStageBytes : 2 * kRouteBuf;
+  static_assert(kWaves16 * 16 * D * 2 <= kRegionA, "epilogue staging fits in the stage buffers");
+  constexpr int kStagesPerBlock = BLK / kStage;
+  uint32_t* umask = (uint32_t*)(smem_raw + kRegionA);  // [W]: union of the tile's rows
+  const int W = (int)(a.Mp / 32);
+
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform, in scalar registers
+  const int lane = t & 63, q = lane & 15, g = lane >> 4;
+  const int64_t ntiles = (a.N + QT - 1) / QT;
+  int64_t w;
+  if (!work_item(a.BH * ntiles, w)) return;
+  const int64_t bh = w / ntiles;
+  const int64_t tile = w % ntiles;
+  const int64_t row0 = tile * QT + wave * 16;  // first row of this wave
+  const int64_t row = row0 + q;
+  const bool rvalid = row < a.N;
+
+  const uint16_t* qb = a.q + a.in.base(bh);
+  const uint16_t* kb = a.k + a.in.base(bh);
+  const uint16_t* vb = a.v + a.in.base(bh);
+  const int64_t sn = a.in.sn;
+  uint32_t* rmask = a.rowmask + bh * W * a.N;  // word w of row r at rmask[w * N + r]
+
+  bf16x8 qf[D / 32];
+  load_q16<D>(qb + row * sn, rvalid, qf);
+  // padding rows keep nothing; with a caller's selection the threshold is not used
+  const float tau = (rvalid && !a.mask_in) ? a.tau[bh * a.N + row] : INFINITY;
+  // s >= tau  <=>  raw dot product >= tau * sqrt(d)  (compared in fp32)
+  const float tau_raw = tau * sqrtf((float)D);
+
+  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+  const float sl2 = inv_sqrt_d * kLog2e;
+  const int n_last = (int)(a.N - (a.M - 1) * (int64_t)a.block);
+  const float l2n_full = log2f((float)a.block);
+  const float l2n_last = log2f((float)n_last);
+
+  for (int i = t; i < W; i += NT) umask[i] = 0u;
+
+  // ---- pooled sweep: selection bits, tile union, pooled tokens ----
+  const int64_t piece = a.BH * a.Mp * D;
+  const uint16_t* kp0 = a.kp + bh * a.Mp * D;  // hi; mid at + piece, lo at + 2 piece
+  const uint16_t* vt0 = a.vbt + bh * D * a.Mp;
+  f32x4 o[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrun = -1e30f;  // running max, log2 domain
+  float lsum = 0.f;
+  const int nchunks = (int)(a.Mp / 32);
+  const TileOffsets<D, 32, NT> coff(D);
+  const VbtOffsets<D, NT> voff(a.Mp);
+  auto issue_chunk = [&](int cb, int b) {
+    lds_u8* base = smem + b * kRouteBuf;
+    load_dense_rows<D, 32, NT>(kp0 + 2 * piece, (int64_t)cb * 32, coff, base);
+    load_dense_rows<D, 32, NT>(kp0 + 1 * piece, (int64_t)cb * 32, coff, base + kChunkTile);
+    load_dense_rows<D, 32, NT>(kp0, (int64_t)cb * 32, coff, base + 2 * kChunkTile);
+    load_vbt_buf<D, NT>(vt0, a.Mp, cb, voff, base + 3 * kChunkTile);
+  };
+  const uint32_t* min_row = a.mask_in ? a.mask_in + (bh * a.N + row) * W : nullptr;
+  auto in_word = [&](int cb) -> uint32_t { return (min_row && rvalid) ? min_row[cb] : 0u; };
+  issue_chunk(0, 0);
+  uint32_t win_next = in_word(0);
+  for (int cb = 0; cb < nchunks; ++cb) {
+    const int b = cb & 1;
+    wait_vmcnt<0>();
+    bar();  // publishes chunk cb, retires chunk cb - 1's buffer
+    const uint32_t win = win_next;
+    if (cb + 1 < nchunks) {
+      issue_chunk(cb + 1, b ^ 1);
+      win_next = in_word(cb + 1);
+    }
+    const lds_u8* base = smem + b * kRouteBuf;
+    const int lane_v = fresh_lane();
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int bt = 0; bt < 2; ++bt)
+        acc[bt] = scores16<D>(base + p * kChunkTile, 16 * bt, qf, acc[bt], lane_v);
+    // register (bt, i) of lane row g holds block 16 bt + 4 g + i of the chunk
+    uint32_t bits = 0u;
+    float x[2][4];
+    float cmax = -INFINITY;
+    const int nvalid = (int)(a.M - (int64_t)cb * 32);  // blocks of this chunk below M
+#pragma unroll
+    for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kj = 16 * bt + 4 * g + i;
+        const bool valid = kj < nvalid;
+        const bool sel = valid && (min_row ? ((win >> kj) & 1u) != 0u : acc[bt][i] >= tau_raw);
+        bits |= (sel ? 1u : 0u) << kj;
+        x[bt][i] = (valid && !sel)
+                       ? fmaf(acc[bt][i], sl2, kj == nvalid - 1 ? l2n_last : l2n_full)
+                       : -INFINITY;
+        cmax = fmaxf(cmax, x[bt][i]);
+      }
+    const uint32_t word = quad_or(bits);
+    if (g == 0 && rvalid) {
+      rmask[(int64_t)cb * a.N + row] = word;
+      if (a.mask_out) a.mask_out[(bh * a.N + row) * W + cb] = word;
+    }
+    if (g == 0 && word) atomicOr(&umask[cb], word);
+    if (!a.drop) {
+      cmax = quad_max(cmax);
+      raise_max16<D>(cmax, true, mrun, lsum, o);
+      uint32_t pk[4];
+#pragma unroll
+      for (int bt = 0; bt < 2; ++bt) {
+        const float p0 = __builtin_amdgcn_exp2f(x[bt][0] - mrun);
+        const float p1 = __builtin_amdgcn_exp2f(x[bt][1] - mrun);
+        const float p2 = __builtin_amdgcn_exp2f(x[bt][2] - mrun);
+        const float p3 = __builtin_amdgcn_exp2f(x[bt][3] - mrun);
+        pk[2 * bt] = pack_bf16x2(p0, p1);
+        pk[2 * bt + 1] = pack_bf16x2(p2, p3);
+        lsum = add_bf16x2(pk[2 * bt], lsum);
+        lsum = add_bf16x2(pk[2 * bt + 1], lsum);
+      }
+      pv_pooled16<D>(base + 3 * kChunkTile, p_operand16(pk), o, lane_v);
+    }
+  }
+  __syncthreads();  // union complete and chunk buffers retired before the exact loop
+
+  // ---- exact attention over the kept blocks, double-buffered 64-key stages ----
+  int it_w = -1;
+  uint32_t it_u = 0u;
+  int it_j = -1, it_s = kStagesPerBlock;
+  auto next_stage = [&](int& j, int& s) -> bool {
+    for (;;) {
+      if (it_j >= 0 && it_s + 1 < kStagesPerBlock && it_j * BLK + (it_s + 1) * kStage < (int)a.N) {
+        ++it_s;
+        j = it_j;
+        s = it_s;
+        return true;
+      }
+      while (it_u == 0u) {
+        if (++it_w >= W) return false;
+        it_u = __builtin_amdgcn_readfirstlane(umask[it_w]);
+      }
+      const int b = __builtin_ctz(it_u);
+      it_u &= it_u - 1u;
+      it_j = it_w * 32 + b;
+      it_s = -1;
+    }
+  };
+  // copy offsets recomputed per stage (see fresh_lane)
+  auto issue = [&](int j, int s, int buf) {
+    const int64_t r0 = (int64_t)j * BLK + s * kStage;
+    lds_u8* base = smem + buf * kStageBytes;
+    const TileOffsets<D, kStage, NT> toff(sn, wave * 64 + fresh_lane());
+    load_rows<D, kStage, NT>(kb, r0, a.N, sn, toff, base);
+    load_rows<D, kStage, NT>(vb, r0, a.N, sn, toff, base + kTileBytes);
+  };
+  // selection words through a buffer resource: scalar word offset, 32-bit lane offset
+  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      rmask, (short)0, (int)((int64_t)W * a.N * 4), 0x00020000);
+  const uint32_t wvoff = (uint32_t)(row * 4);
+  auto load_word = [&](int wd) -> uint32_t {
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)wd * a.N * 4));
+    return rvalid ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(wrsrc, wvoff, soff, 0) : 0u;
+  };
+  int cur_j = -1, cur_s = 0;
+  bool have = next_stage(cur_j, cur_s);
+  int mask_w = -1;
+  uint32_t mask_word = 0u;
+  if (have) {
+    issue(cur_j, cur_s, 0);
+    mask_w = cur_j >> 5;
+    mask_word = load_word(mask_w);
+  }
+  int buf = 0;
+  while (have) {
+    wait_vmcnt<0>();
+    bar();  // publishes this stage's copy and retires the previous stage's buffer
+    int nj = -1, ns = 0;
+    const bool more = next_stage(nj, ns);
+    int next_w = mask_w;
+    uint32_t next_word = mask_word;
+    if (more) {
+      issue(nj, ns, buf ^ 1);
+      if ((nj >> 5) != mask_w) {
+        next_w = nj >> 5;
+        next_word = load_word(next_w);
+      }
+    }
+    const bool active = (mask_word >> (cur_j & 31)) & 1u;
+    const int r0 = cur_j * BLK + cur_s * kStage;
+    const int nvalid = (int)a.N - r0 < kStage ? (int)a.N - r0 : kStage;
+    const lds_u8* base = smem + buf * kStageBytes;
+    // a wave none of whose 16 rows keeps the block skips the stage's math
+    if (__builtin_amdgcn_ballot_w64(active))
+      exact_stage16<D>(base, base + kTileBytes, qf, active, nvalid, sl2, mrun, lsum, o,
+                       fresh_lane());
+    buf ^= 1;
+    cur_j = nj;
+    cur_s = ns;
+    mask_w = next_w;
+    mask_word = next_word;
+    have = more;
+  }
+  if (a.tile_kept && t == 0) {  // blocks kept by some row of the tile
+    int kept = 0;
+    for (int i = 0; i < W; ++i) kept += __builtin_popcount(umask[i]);
+    a.tile_kept[bh * ntiles + tile] = kept;
+  }
+  bar();  // every wave is done with the stage buffers before the epilogue reuses them
+
+  epilogue16<D>(o, mrun, lsum, row0, a.N, a.out + a.outs.base(bh), a.outs.sn,
+                a.out_f32 ? a.out_f32 + bh * a.N * D : nullptr, a.lse ? a.lse + bh * a.N : nullptr,
+                smem + wave * 16 * D * 2);
+}
+
 // Half HB of stage n of the pipelined exact loop over consecutive stages (dense kernel); B = n & 1.
 // NEXT: a next 32-key block exists (it may be partial).  sc holds the current block's scores,
 // sn receives the next block's.  K tiles live at kbuf + b * tile, V tiles at vbuf + b * tile.
@@ -980,11 +1450,12 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_map_kernel(const uint16_t* 
   const int64_t row0 = tile * kQTile + wave * 32;
   float* stage = (float*)(smem_raw + 2 * kBuf) + wave * 32 * kStageStride;  // this wave's 32 x 32
   const int nchunks = (int)(Mp / 32);
+  const TileOffsets<D, 32> coff(D);
   auto issue_chunk = [&](int cb, int b) {
     lds_u8* base = smem + b * kBuf;
-    load_tile<D, 32>(kp0 + 2 * piece, (int64_t)cb * 32, Mp, base);
-    load_tile<D, 32>(kp0 + 1 * piece, (int64_t)cb * 32, Mp, base + kChunkTile);
-    load_tile<D, 32>(kp0, (int64_t)cb * 32, Mp, base + 2 * kChunkTile);
+    load_dense_rows<D, 32>(kp0 + 2 * piece, (int64_t)cb * 32, coff, base);
+    load_dense_rows<D, 32>(kp0 + 1 * piece, (int64_t)cb * 32, coff, base + kChunkTile);
+    load_dense_rows<D, 32>(kp0, (int64_t)cb * 32, coff, base + 2 * kChunkTile);
   };
   issue_chunk(0, 0);
   for (int cb = 0; cb < nchunks; ++cb) {
@@ -1133,11 +1604,22 @@ static hipError_t launch_sparse_t(const SparseArgs& a, hipStream_t stream) {
 // Four waves per workgroup and two workgroups per CU: measured at the Wan2.1-14B shape, eight
 // waves (one workgroup per CU, each copy shared by twice the rows) were 9% slower -- the second
 // workgroup's independent progress is worth more than the halved copy traffic.
+template <int D, int BLK>
+static hipError_t launch_sparse16_t(const SparseArgs& a, hipStream_t stream) {
+  const size_t smem = sparse_smem_bytes(D, a.Mp, 1);
+  auto kern = sol_attn16_kernel<D, BLK>;
+  hipError_t err = set_smem(kern, smem);
+  if (err != hipSuccess) return err;
+  const int64_t ntiles = (a.N + kQTile - 1) / kQTile;
+  hipLaunchKernelGGL(kern, dim3(xcd_grid(a.BH * ntiles)), dim3(kThreads16), smem, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_sparse(int d, const SparseArgs& a, hipStream_t stream) {
   if (d == 64 && a.block == 64) return launch_sparse_t<64, 64, 4>(a, stream);
   if (d == 64 && a.block == 128) return launch_sparse_t<64, 128, 4>(a, stream);
-  if (d == 128 && a.block == 64) return launch_sparse_t<128, 64, 4>(a, stream);
-  return launch_sparse_t<128, 128, 4>(a, stream);
+  if (d == 128 && a.block == 64) return launch_sparse16_t<128, 64>(a, stream);
+  return launch_sparse16_t<128, 128>(a, stream);
 }
 
 template <int D>

@@ -34,6 +34,14 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x32_bf16: lane l = 16*g + q (g = l >> 4 the lane row, q = l & 15).
+//   A operand (16 x 32): lane l holds A[q][8g .. 8g + 7]; B operand (32 x 16): B[8g .. 8g + 7][q].
+//   Result (16 x 16, 4 fp32 per lane): lane l holds D[4g + i][q], i = 0..3.
+// As with the 32x32 form, A and B only have to agree on which k indices lane row g holds.
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // bf16 <-> fp32 bit helpers (round to nearest even; inputs here are finite).
 __device__ __forceinline__ uint32_t f32_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ __forceinline__ float bits_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
@@ -89,6 +97,30 @@ __device__ __forceinline__ uint32_t pair_or(uint32_t x) {
   uint32_t a, b;
   pair_values(x, a, b);
   return a | b;
+}
+
+// Combines over the four 16-lane rows holding one column of a 16x16 result (lanes q, q + 16,
+// q + 32, q + 48): v_permlane16_swap pairs lane l with l ^ 16 the way permlane32_swap pairs l with
+// l ^ 32, so two swaps give the four-way value in every lane.
+__device__ __forceinline__ void row_pair_values(uint32_t x, uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  a = r[0];
+  b = r[1];
+}
+__device__ __forceinline__ float quad_max(float x) {
+  uint32_t a, b;
+  row_pair_values(__builtin_bit_cast(uint32_t, x), a, b);
+  return pair_max(fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  uint32_t a, b;
+  row_pair_values(__builtin_bit_cast(uint32_t, x), a, b);
+  return pair_sum(__builtin_bit_cast(float, a) + __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ uint32_t quad_or(uint32_t x) {
+  uint32_t a, b;
+  row_pair_values(x, a, b);
+  return pair_or(a | b);
 }
 
 }  // namespace solattn
