@@ -985,32 +985,6 @@ __device__ __forceinline__ bf16x8 p_operand16(const uint32_t (&pk)[4]) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// O^T[dt] += V^T P^T for one 32-key group (tile rows kr0 .. kr0 + 31 of a V tile).  The A operand
-// of lane (g, q) is V^T[16 dt + q][keys 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3 of the group]:
-// two LDS transpose reads, in which the 16 lanes of row g point at the four key rows (lane / 4)
-// and four column quads (lane % 4) and lane q receives column q of those rows.
-template <int D>
-__device__ __forceinline__ void pv16(const lds_u8* vtile, int kr0, const bf16x8& b,
-                                     f32x4 (&o)[D / 16], int lane) {
-  const int j = lane & 15, g = lane >> 4;
-  const int r1 = kr0 + 4 * g + (j >> 2), r2 = r1 + 16;
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
-    const int c = 16 * dt + 4 * (j & 3);
-    const int half = ((c >> 2) & 1) * 8;
-    const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(vtile + tile_off<D>(r1, c >> 3) + half));
-    const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(vtile + tile_off<D>(r2, c >> 3) + half));
-    u32x4 raw;
-    raw[0] = __builtin_bit_cast(u32x2, x0)[0];
-    raw[1] = __builtin_bit_cast(u32x2, x0)[1];
-    raw[2] = __builtin_bit_cast(u32x2, x1)[0];
-    raw[3] = __builtin_bit_cast(u32x2, x1)[1];
-    o[dt] = mfma16(__builtin_bit_cast(bf16x8, raw), b, o[dt]);
-  }
-}
-
 // O^T[dt] += Vbar^T P^T for the 32 pooled blocks of a routing chunk: the A operand of lane (g, q)
 // is row 16 dt + q of the Vbar^T chunk tile at blocks 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3,
 // two 8-byte reads.
@@ -1059,15 +1033,33 @@ __device__ __forceinline__ void exact_stage16(const lds_u8* ktile, const lds_u8*
                                               float sl2, float& mrun, float& lsum,
                                               f32x4 (&o)[D / 16], int lane) {
   constexpr int NT16 = kStage / 16;  // 16-key score tiles per stage
-  const int g = lane >> 4;
+  constexpr int KS = D / 32;         // k steps per tile
+  const int q = lane & 15, g = lane >> 4;
+  // Q.K^T, software-pipelined by hand: the operand reads of tile kt + 1 are issued before tile
+  // kt's matrix instructions, so two tiles' reads are in flight at most
   f32x4 s[NT16];
-  // scheduling fences between tiles keep at most one tile's operand reads in flight (register
-  // budget of four waves per SIMD)
+  u32x4 kr[2][KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) kr[0][kk] = lds_read16(ktile + tile_off<D>(q, kk + KS * g));
 #pragma unroll
   for (int kt = 0; kt < NT16; ++kt) {
-    s[kt] = scores16<D>(ktile, 16 * kt, qf, f32x4{0.f, 0.f, 0.f, 0.f}, lane);
-    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < NT16) {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        kr[(kt + 1) & 1][kk] = lds_read16(ktile + tile_off<D>(16 * (kt + 1) + q, kk + KS * g));
+    }
+    s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) s[kt] = mfma16(__builtin_bit_cast(bf16x8, kr[kt & 1][kk]), qf[kk], s[kt]);
   }
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, KS, 0);
+#pragma unroll
+  for (int kt = 0; kt + 1 < NT16; ++kt) {
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, KS, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, KS, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSgMfma, KS, 0);
+  __builtin_amdgcn_sched_barrier(0);
   if (nvalid < kStage) {  // wave-uniform
 #pragma unroll
     for (int kt = 0; kt < NT16; ++kt)
@@ -1085,9 +1077,9 @@ __device__ __forceinline__ void exact_stage16(const lds_u8* ktile, const lds_u8*
   // rows that do not take part subtract +inf: every probability is 0
   const float moff = active ? -mrun : -INFINITY;
   float ps = 0.f;
+  uint32_t pk[NT16 / 2][4];
 #pragma unroll
   for (int grp = 0; grp < NT16 / 2; ++grp) {
-    uint32_t pk[4];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       const f32x4& sv = s[2 * grp + h2];
@@ -1095,15 +1087,51 @@ __device__ __forceinline__ void exact_stage16(const lds_u8* ktile, const lds_u8*
       const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[1], sl2, moff));
       const float p2 = __builtin_amdgcn_exp2f(fmaf(sv[2], sl2, moff));
       const float p3 = __builtin_amdgcn_exp2f(fmaf(sv[3], sl2, moff));
-      pk[2 * h2] = pack_bf16x2(p0, p1);
-      pk[2 * h2 + 1] = pack_bf16x2(p2, p3);
-      ps = add_bf16x2(pk[2 * h2], ps);
-      ps = add_bf16x2(pk[2 * h2 + 1], ps);
+      pk[grp][2 * h2] = pack_bf16x2(p0, p1);
+      pk[grp][2 * h2 + 1] = pack_bf16x2(p2, p3);
+      ps = add_bf16x2(pk[grp][2 * h2], ps);
+      ps = add_bf16x2(pk[grp][2 * h2 + 1], ps);
     }
-    pv16<D>(vtile, 32 * grp, p_operand16(pk), o, lane);
-    __builtin_amdgcn_sched_barrier(0);
   }
   lsum += ps;
+  // O^T[dt] += V^T P^T, 2 x D/16 matrix instructions, the reads of the next one issued before the
+  // current one.  For 32-key group grp, the A operand of lane (g, q) is V^T[16 dt + q][keys
+  // 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3 of the group]: two LDS transpose reads, in which the
+  // 16 lanes of row g point at the four key rows (lane / 4) and four column quads (lane % 4) and
+  // lane q receives column q of those rows.
+  const int j = q;
+  constexpr int NPV = (NT16 / 2) * (D / 16);
+  s16x4 vr[2][2];
+  auto read_v = [&](int idx, s16x4 (&dst)[2]) {
+    const int grp = idx / (D / 16), dt = idx % (D / 16);
+    const int r1 = 32 * grp + 4 * g + (j >> 2);
+    const int c = 16 * dt + 4 * (j & 3);
+    const int half = ((c >> 2) & 1) * 8;
+    dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(vtile + tile_off<D>(r1, c >> 3) + half));
+    dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(vtile + tile_off<D>(r1 + 16, c >> 3) + half));
+  };
+  read_v(0, vr[0]);
+#pragma unroll
+  for (int idx = 0; idx < NPV; ++idx) {
+    if (idx + 1 < NPV) read_v(idx + 1, vr[(idx + 1) & 1]);
+    const int grp = idx / (D / 16), dt = idx % (D / 16);
+    u32x4 raw;
+    raw[0] = __builtin_bit_cast(u32x2, vr[idx & 1][0])[0];
+    raw[1] = __builtin_bit_cast(u32x2, vr[idx & 1][0])[1];
+    raw[2] = __builtin_bit_cast(u32x2, vr[idx & 1][1])[0];
+    raw[3] = __builtin_bit_cast(u32x2, vr[idx & 1][1])[1];
+    o[dt] = mfma16(__builtin_bit_cast(bf16x8, raw), p_operand16(pk[grp]), o[dt]);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+#pragma unroll
+  for (int idx = 0; idx + 1 < NPV; ++idx) {
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Write O = O^T / l for the wave's 16 rows through LDS (row-major, swizzled) so that every global
