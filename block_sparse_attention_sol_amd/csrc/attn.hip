@@ -756,8 +756,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void sol_attn_kernel(SparseA
     load_vbt_buf<D, NT>(vt0, a.Mp, cb, voff, base + 3 * kChunkTile);
   };
   // the caller's selection word of this row for chunk cb (loaded one chunk ahead, with the copy)
-  const uint32_t* min_row = a.mask_in ? a.mask_in + (bh * a.N + row) * W : nullptr;
-  auto in_word = [&](int cb) -> uint32_t { return (min_row && rvalid) ? min_row[cb] : 0u; };
+  const bool has_in = a.mask_in != nullptr;  // wave-uniform
+  const uint32_t* min_row = has_in ? a.mask_in + (bh * a.N + row) * W : nullptr;
+  auto in_word = [&](int cb) -> uint32_t { return (has_in && rvalid) ? min_row[cb] : 0u; };
   issue_chunk(0, 0);
   uint32_t win_next = in_word(0);
   for (int cb = 0; cb < nchunks; ++cb) {
@@ -781,7 +782,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void sol_attn_kernel(SparseA
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int kj = key_of(v, h);
-        const bool sel = min_row ? ((win >> kj) & 1u) != 0u : acc[v] >= tau_raw;
+        const bool sel = has_in ? ((win >> kj) & 1u) != 0u : acc[v] >= tau_raw;
         bits |= (sel ? 1u : 0u) << kj;
         x[v] = sel ? -INFINITY : fmaf(acc[v], sl2, l2n_full);
         cmax = fmaxf(cmax, x[v]);
@@ -791,10 +792,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void sol_attn_kernel(SparseA
       for (int v = 0; v < 16; ++v) {
         const int kj = key_of(v, h);
         const bool valid = kj < nvalid;
-        const bool sel = valid && (min_row ? ((win >> kj) & 1u) != 0u : acc[v] >= tau_raw);
+        const bool sel = valid & (has_in ? ((win >> kj) & 1u) != 0u : acc[v] >= tau_raw);
         bits |= (sel ? 1u : 0u) << kj;
-        x[v] = (valid && !sel) ? fmaf(acc[v], sl2, kj == nvalid - 1 ? l2n_last : l2n_full)
-                               : -INFINITY;
+        x[v] = (valid & !sel) ? fmaf(acc[v], sl2, kj == nvalid - 1 ? l2n_last : l2n_full)
+                              : -INFINITY;
         cmax = fmaxf(cmax, x[v]);
       }
     }
@@ -1241,8 +1242,9 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     load_dense_rows<D, 32, NT>(kp0, (int64_t)cb * 32, coff, base + 2 * kChunkTile);
     load_vbt_buf<D, NT>(vt0, a.Mp, cb, voff, base + 3 * kChunkTile);
   };
-  const uint32_t* min_row = a.mask_in ? a.mask_in + (bh * a.N + row) * W : nullptr;
-  auto in_word = [&](int cb) -> uint32_t { return (min_row && rvalid) ? min_row[cb] : 0u; };
+  const bool has_in = a.mask_in != nullptr;  // wave-uniform
+  const uint32_t* min_row = has_in ? a.mask_in + (bh * a.N + row) * W : nullptr;
+  auto in_word = [&](int cb) -> uint32_t { return (has_in && rvalid) ? min_row[cb] : 0u; };
   issue_chunk(0, 0);
   uint32_t win_next = in_word(0);
   for (int cb = 0; cb < nchunks; ++cb) {
@@ -1256,30 +1258,65 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     }
     const lds_u8* base = smem + b * kRouteBuf;
     const int lane_v = fresh_lane();
+    const int qv = lane_v & 15, gv = lane_v >> 4;
+    // proxies: 6 (piece, block tile) steps of D/32 matrix instructions, pieces smallest first; the
+    // reads of step st + 1 are issued before step st's matrix instructions
+    constexpr int KS = D / 32;
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    u32x4 kr[2][KS];
+    auto read_step = [&](int st, u32x4 (&dst)[KS]) {
+      const lds_u8* tl = base + (st >> 1) * kChunkTile;
 #pragma unroll
-    for (int p = 0; p < 3; ++p)
+      for (int kk = 0; kk < KS; ++kk)
+        dst[kk] = lds_read16(tl + tile_off<D>(16 * (st & 1) + qv, kk + KS * gv));
+    };
+    read_step(0, kr[0]);
 #pragma unroll
-      for (int bt = 0; bt < 2; ++bt)
-        acc[bt] = scores16<D>(base + p * kChunkTile, 16 * bt, qf, acc[bt], lane_v);
+    for (int st = 0; st < 6; ++st) {
+      if (st + 1 < 6) read_step(st + 1, kr[(st + 1) & 1]);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        acc[st & 1] = mfma16(__builtin_bit_cast(bf16x8, kr[st & 1][kk]), qf[kk], acc[st & 1]);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, KS, 0);
+#pragma unroll
+    for (int st = 0; st + 1 < 6; ++st) {
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, KS, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, KS, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, KS, 0);
+    __builtin_amdgcn_sched_barrier(0);
     // register (bt, i) of lane row g holds block 16 bt + 4 g + i of the chunk
     uint32_t bits = 0u;
     float x[2][4];
     float cmax = -INFINITY;
     const int nvalid = (int)(a.M - (int64_t)cb * 32);  // blocks of this chunk below M
+    if (nvalid >= 32) {  // wave-uniform: every block of the chunk exists and is full-size
 #pragma unroll
-    for (int bt = 0; bt < 2; ++bt)
+      for (int bt = 0; bt < 2; ++bt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kj = 16 * bt + 4 * g + i;
-        const bool valid = kj < nvalid;
-        const bool sel = valid && (min_row ? ((win >> kj) & 1u) != 0u : acc[bt][i] >= tau_raw);
-        bits |= (sel ? 1u : 0u) << kj;
-        x[bt][i] = (valid && !sel)
-                       ? fmaf(acc[bt][i], sl2, kj == nvalid - 1 ? l2n_last : l2n_full)
-                       : -INFINITY;
-        cmax = fmaxf(cmax, x[bt][i]);
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int kj = 16 * bt + 4 * g + i;
+          const bool sel = has_in ? ((win >> kj) & 1u) != 0u : acc[bt][i] >= tau_raw;
+          bits |= (sel ? 1u : 0u) << kj;
+          x[bt][i] = sel ? -INFINITY : fmaf(acc[bt][i], sl2, l2n_full);
+          cmax = fmaxf(cmax, x[bt][i]);
+        }
+    } else {
+#pragma unroll
+      for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kj = 16 * bt + 4 * g + i;
+          const bool valid = kj < nvalid;
+          const bool sel = valid & (has_in ? ((win >> kj) & 1u) != 0u : acc[bt][i] >= tau_raw);
+          bits |= (sel ? 1u : 0u) << kj;
+          x[bt][i] = (valid & !sel)
+                         ? fmaf(acc[bt][i], sl2, kj == nvalid - 1 ? l2n_last : l2n_full)
+                         : -INFINITY;
+          cmax = fmaxf(cmax, x[bt][i]);
+        }
+    }
     const uint32_t word = quad_or(bits);
     if (g == 0 && rvalid) {
       rmask[(int64_t)cb * a.N + row] = word;
