@@ -195,6 +195,20 @@ __device__ __forceinline__ void load_rows(const uint16_t* base, int64_t r0, int6
 // before the barrier), so the fence's wait for every outstanding load -- including the next
 // stage's prefetch -- is not wanted.  The empty asm statements keep the compiler from moving
 // memory accesses across it.
+// Share k of the copy load_rows makes of rows [r0, r0 + ROWS) (the loads lane l of wave k issues
+// there), issued by the calling wave instead; k is wave-uniform.
+template <int D, int ROWS, int NT>
+__device__ __forceinline__ void load_rows_share(const uint16_t* base, int64_t r0, int64_t limit,
+                                                int64_t sn, int k, int lane, lds_u8* tile) {
+  const int64_t rest = (limit - r0 - 1) * sn * 2 + D * 2;
+  const uint32_t bytes = (uint32_t)(rest < 0xffffffffll ? rest : 0xffffffffll);
+  const i32x4_t rsrc = make_rsrc(base + r0 * sn, bytes);
+  const TileOffsets<D, ROWS, NT> off(sn, k * 64 + lane);
+#pragma unroll
+  for (int i = 0; i < tile_loads<D, ROWS, NT>(); ++i)
+    dma16(rsrc, off.v[i], 0u, tile + (i * NT + k * 64) * 16);
+}
+
 __device__ __forceinline__ void bar() {
   __asm__ __volatile__("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -1189,6 +1203,7 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
   constexpr int kStagesPerBlock = BLK / kStage;
   uint32_t* umask = (uint32_t*)(smem_raw + kRegionA);  // [W]: union of the tile's rows
   const int W = (int)(a.Mp / 32);
+  uint32_t* wmask = umask + W;                         // [kWaves16][W]: union of each wave's rows
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform, in scalar registers
@@ -1221,7 +1236,7 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
   const float l2n_full = log2f((float)a.block);
   const float l2n_last = log2f((float)n_last);
 
-  for (int i = t; i < W; i += NT) umask[i] = 0u;
+  for (int i = t; i < (1 + kWaves16) * W; i += NT) umask[i] = 0u;
 
   // ---- pooled sweep: selection bits, tile union, pooled tokens ----
   const int64_t piece = a.BH * a.Mp * D;
@@ -1322,7 +1337,10 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
       rmask[(int64_t)cb * a.N + row] = word;
       if (a.mask_out) a.mask_out[(bh * a.N + row) * W + cb] = word;
     }
-    if (g == 0 && word) atomicOr(&umask[cb], word);
+    if (g == 0 && word) {
+      atomicOr(&umask[cb], word);
+      atomicOr(&wmask[wave * W + cb], word);
+    }
     if (!a.drop) {
       cmax = quad_max(cmax);
       raise_max16<D>(cmax, true, mrun, lsum, o);
@@ -1344,15 +1362,18 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
   __syncthreads();  // union complete and chunk buffers retired before the exact loop
 
   // ---- exact attention over the kept blocks, double-buffered 64-key stages ----
+  // Stage iterator over the union, with the set of waves that have math in each stage (bit w:
+  // some row of wave w keeps the block).  All values are wave-uniform.
   int it_w = -1;
-  uint32_t it_u = 0u;
+  uint32_t it_u = 0u, it_act = 0u;
   int it_j = -1, it_s = kStagesPerBlock;
-  auto next_stage = [&](int& j, int& s) -> bool {
+  auto next_stage = [&](int& j, int& s, uint32_t& act) -> bool {
     for (;;) {
       if (it_j >= 0 && it_s + 1 < kStagesPerBlock && it_j * BLK + (it_s + 1) * kStage < (int)a.N) {
         ++it_s;
         j = it_j;
         s = it_s;
+        act = it_act;
         return true;
       }
       while (it_u == 0u) {
@@ -1363,15 +1384,33 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
       it_u &= it_u - 1u;
       it_j = it_w * 32 + b;
       it_s = -1;
+      // the waves' selection words for this block (one LDS word per wave, lane w reads wave w's)
+      const uint32_t ww = lane < kWaves16 ? wmask[lane * W + it_w] : 0u;
+      it_act = (uint32_t)__builtin_amdgcn_ballot_w64(((ww >> b) & 1u) != 0u);
     }
   };
-  // copy offsets recomputed per stage (see fresh_lane)
-  auto issue = [&](int j, int s, int buf) {
+  // The next stage's copy, issued during a stage whose waves with math are `act`: when some wave
+  // has none, the idle waves issue the whole copy between them (wave share k to the (k mod
+  // #idle)-th idle wave), so that the waves that compute do not queue behind the copy's issue.
+  // Copy offsets are recomputed per stage (see fresh_lane).
+  auto issue = [&](int j, int s, int buf, uint32_t act) {
     const int64_t r0 = (int64_t)j * BLK + s * kStage;
     lds_u8* base = smem + buf * kStageBytes;
-    const TileOffsets<D, kStage, NT> toff(sn, wave * 64 + fresh_lane());
-    load_rows<D, kStage, NT>(kb, r0, a.N, sn, toff, base);
-    load_rows<D, kStage, NT>(vb, r0, a.N, sn, toff, base + kTileBytes);
+    const uint32_t idle = ~act & ((1u << kWaves16) - 1u);
+    const int lane_v = fresh_lane();
+    if (idle == 0u) {
+      load_rows_share<D, kStage, NT>(kb, r0, a.N, sn, wave, lane_v, base);
+      load_rows_share<D, kStage, NT>(vb, r0, a.N, sn, wave, lane_v, base + kTileBytes);
+      return;
+    }
+    if (!((idle >> wave) & 1u)) return;
+    const int nidle = __builtin_popcount(idle);
+    const int rank = __builtin_popcount(idle & ((1u << wave) - 1u));
+    for (int k = rank; k < kWaves16; k += nidle) {
+      const int ku = __builtin_amdgcn_readfirstlane(k);
+      load_rows_share<D, kStage, NT>(kb, r0, a.N, sn, ku, lane_v, base);
+      load_rows_share<D, kStage, NT>(vb, r0, a.N, sn, ku, lane_v, base + kTileBytes);
+    }
   };
   // selection words through a buffer resource: scalar word offset, 32-bit lane offset
   const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -1382,11 +1421,12 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     return rvalid ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(wrsrc, wvoff, soff, 0) : 0u;
   };
   int cur_j = -1, cur_s = 0;
-  bool have = next_stage(cur_j, cur_s);
+  uint32_t cur_act = 0u;
+  bool have = next_stage(cur_j, cur_s, cur_act);
   int mask_w = -1;
   uint32_t mask_word = 0u;
   if (have) {
-    issue(cur_j, cur_s, 0);
+    issue(cur_j, cur_s, 0, 0u);  // before the loop every wave takes its own share
     mask_w = cur_j >> 5;
     mask_word = load_word(mask_w);
   }
@@ -1395,11 +1435,12 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     wait_vmcnt<0>();
     bar();  // publishes this stage's copy and retires the previous stage's buffer
     int nj = -1, ns = 0;
-    const bool more = next_stage(nj, ns);
+    uint32_t nact = 0u;
+    const bool more = next_stage(nj, ns, nact);
     int next_w = mask_w;
     uint32_t next_word = mask_word;
     if (more) {
-      issue(nj, ns, buf ^ 1);
+      issue(nj, ns, buf ^ 1, cur_act);
       if ((nj >> 5) != mask_w) {
         next_w = nj >> 5;
         next_word = load_word(next_w);
@@ -1416,6 +1457,7 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     buf ^= 1;
     cur_j = nj;
     cur_s = ns;
+    cur_act = nact;
     mask_w = next_w;
     mask_word = next_word;
     have = more;
@@ -1671,7 +1713,7 @@ static hipError_t launch_sparse_t(const SparseArgs& a, hipStream_t stream) {
 // workgroup's independent progress is worth more than the halved copy traffic.
 template <int D, int BLK>
 static hipError_t launch_sparse16_t(const SparseArgs& a, hipStream_t stream) {
-  const size_t smem = sparse_smem_bytes(D, a.Mp, 1);
+  const size_t smem = sparse_smem_bytes(D, a.Mp, 1) + (size_t)kWaves16 * (a.Mp / 32) * 4;
   auto kern = sol_attn16_kernel<D, BLK>;
   hipError_t err = set_smem(kern, smem);
   if (err != hipSuccess) return err;
