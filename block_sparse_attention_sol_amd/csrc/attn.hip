@@ -1366,6 +1366,7 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
   // some row of wave w keeps the block).  All values are wave-uniform.
   int it_w = -1;
   uint32_t it_u = 0u, it_act = 0u;
+  uint32_t it_ww = 0u;  // lane w < kWaves16: wave w's selection word for union word it_w
   int it_j = -1, it_s = kStagesPerBlock;
   auto next_stage = [&](int& j, int& s, uint32_t& act) -> bool {
     for (;;) {
@@ -1379,14 +1380,13 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
       while (it_u == 0u) {
         if (++it_w >= W) return false;
         it_u = __builtin_amdgcn_readfirstlane(umask[it_w]);
+        it_ww = lane < kWaves16 ? wmask[lane * W + it_w] : 0u;
       }
       const int b = __builtin_ctz(it_u);
       it_u &= it_u - 1u;
       it_j = it_w * 32 + b;
       it_s = -1;
-      // the waves' selection words for this block (one LDS word per wave, lane w reads wave w's)
-      const uint32_t ww = lane < kWaves16 ? wmask[lane * W + it_w] : 0u;
-      it_act = (uint32_t)__builtin_amdgcn_ballot_w64(((ww >> b) & 1u) != 0u);
+      it_act = (uint32_t)__builtin_amdgcn_ballot_w64(((it_ww >> b) & 1u) != 0u);
     }
   };
   // The next stage's copy, issued during a stage whose waves with math are `act`: when some wave
@@ -1420,6 +1420,8 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)wd * a.N * 4));
     return rvalid ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(wrsrc, wvoff, soff, 0) : 0u;
   };
+  // The iterator runs one stage ahead of the copies: the stage after next is found after this
+  // stage's math, while its last matrix instructions drain.
   int cur_j = -1, cur_s = 0;
   uint32_t cur_act = 0u;
   bool have = next_stage(cur_j, cur_s, cur_act);
@@ -1430,13 +1432,13 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     mask_w = cur_j >> 5;
     mask_word = load_word(mask_w);
   }
+  int nj = -1, ns = 0;
+  uint32_t nact = 0u;
+  bool more = have && next_stage(nj, ns, nact);
   int buf = 0;
   while (have) {
     wait_vmcnt<0>();
     bar();  // publishes this stage's copy and retires the previous stage's buffer
-    int nj = -1, ns = 0;
-    uint32_t nact = 0u;
-    const bool more = next_stage(nj, ns, nact);
     int next_w = mask_w;
     uint32_t next_word = mask_word;
     if (more) {
@@ -1461,6 +1463,7 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     mask_w = next_w;
     mask_word = next_word;
     have = more;
+    if (have) more = next_stage(nj, ns, nact);
   }
   if (a.tile_kept && t == 0) {  // blocks kept by some row of the tile
     int kept = 0;
