@@ -952,6 +952,15 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void sol_attn_kernel(SparseA
 constexpr int kWaves16 = 8;
 constexpr int kThreads16 = 64 * kWaves16;
 
+// OR over lanes 0 .. kWaves16 - 1 of x (the other lanes hold 0), returned in every lane as a
+// wave-uniform value: three butterfly steps within the first 8 lanes, then lane 0's result.
+__device__ __forceinline__ uint32_t union_of_waves(uint32_t x) {
+  x |= (uint32_t)__shfl_xor((int)x, 1);
+  x |= (uint32_t)__shfl_xor((int)x, 2);
+  x |= (uint32_t)__shfl_xor((int)x, 4);
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
 // The lane index, opaque to the optimiser: LDS addresses derived from it inside a loop are
 // recomputed each iteration (a few VALU operations) instead of being hoisted out and held in
 // registers for the whole loop, which at four waves per SIMD (128 VGPRs) would spill.
@@ -1201,9 +1210,8 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
   constexpr int kRegionA = 2 * kStageBytes > 2 * kRouteBuf ? 2 * kStageBytes : 2 * kRouteBuf;
   static_assert(kWaves16 * 16 * D * 2 <= kRegionA, "epilogue staging fits in the stage buffers");
   constexpr int kStagesPerBlock = BLK / kStage;
-  uint32_t* umask = (uint32_t*)(smem_raw + kRegionA);  // [W]: union of the tile's rows
   const int W = (int)(a.Mp / 32);
-  uint32_t* wmask = umask + W;                         // [kWaves16][W]: union of each wave's rows
+  uint32_t* wmask = (uint32_t*)(smem_raw + kRegionA);  // [kWaves16][W]: union of each wave's rows
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform, in scalar registers
@@ -1236,7 +1244,7 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
   const float l2n_full = log2f((float)a.block);
   const float l2n_last = log2f((float)n_last);
 
-  for (int i = t; i < (1 + kWaves16) * W; i += NT) umask[i] = 0u;
+  for (int i = t; i < kWaves16 * W; i += NT) wmask[i] = 0u;
 
   // ---- pooled sweep: selection bits, tile union, pooled tokens ----
   const int64_t piece = a.BH * a.Mp * D;
@@ -1267,10 +1275,6 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     wait_vmcnt<0>();
     bar();  // publishes chunk cb, retires chunk cb - 1's buffer
     const uint32_t win = win_next;
-    if (cb + 1 < nchunks) {
-      issue_chunk(cb + 1, b ^ 1);
-      win_next = in_word(cb + 1);
-    }
     const lds_u8* base = smem + b * kRouteBuf;
     const int lane_v = fresh_lane();
     const int qv = lane_v & 15, gv = lane_v >> 4;
@@ -1301,6 +1305,12 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     }
     __builtin_amdgcn_sched_group_barrier(kSgMfma, KS, 0);
     __builtin_amdgcn_sched_barrier(0);
+    // the next chunk's copy, issued while the proxy matrix instructions drain (every wave has math
+    // here, so a copy issued at the top of the chunk would hold back the whole workgroup)
+    if (cb + 1 < nchunks) {
+      issue_chunk(cb + 1, b ^ 1);
+      win_next = in_word(cb + 1);
+    }
     // register (bt, i) of lane row g holds block 16 bt + 4 g + i of the chunk
     uint32_t bits = 0u;
     float x[2][4];
@@ -1337,10 +1347,7 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
       rmask[(int64_t)cb * a.N + row] = word;
       if (a.mask_out) a.mask_out[(bh * a.N + row) * W + cb] = word;
     }
-    if (g == 0 && word) {
-      atomicOr(&umask[cb], word);
-      atomicOr(&wmask[wave * W + cb], word);
-    }
+    if (g == 0 && word) atomicOr(&wmask[wave * W + cb], word);
     if (!a.drop) {
       cmax = quad_max(cmax);
       raise_max16<D>(cmax, true, mrun, lsum, o);
@@ -1379,8 +1386,8 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
       }
       while (it_u == 0u) {
         if (++it_w >= W) return false;
-        it_u = __builtin_amdgcn_readfirstlane(umask[it_w]);
         it_ww = lane < kWaves16 ? wmask[lane * W + it_w] : 0u;
+        it_u = union_of_waves(it_ww);
       }
       const int b = __builtin_ctz(it_u);
       it_u &= it_u - 1u;
@@ -1465,10 +1472,11 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     have = more;
     if (have) more = next_stage(nj, ns, nact);
   }
-  if (a.tile_kept && t == 0) {  // blocks kept by some row of the tile
+  if (a.tile_kept && wave == 0) {  // blocks kept by some row of the tile
     int kept = 0;
-    for (int i = 0; i < W; ++i) kept += __builtin_popcount(umask[i]);
-    a.tile_kept[bh * ntiles + tile] = kept;
+    for (int i = 0; i < W; ++i)
+      kept += __builtin_popcount(union_of_waves(lane < kWaves16 ? wmask[lane * W + i] : 0u));
+    if (lane == 0) a.tile_kept[bh * ntiles + tile] = kept;
   }
   bar();  // every wave is done with the stage buffers before the epilogue reuses them
 
@@ -1716,7 +1724,7 @@ static hipError_t launch_sparse_t(const SparseArgs& a, hipStream_t stream) {
 // workgroup's independent progress is worth more than the halved copy traffic.
 template <int D, int BLK>
 static hipError_t launch_sparse16_t(const SparseArgs& a, hipStream_t stream) {
-  const size_t smem = sparse_smem_bytes(D, a.Mp, 1) + (size_t)kWaves16 * (a.Mp / 32) * 4;
+  const size_t smem = sparse_smem_bytes(D, a.Mp, 0) + (size_t)kWaves16 * (a.Mp / 32) * 4;
   auto kern = sol_attn16_kernel<D, BLK>;
   hipError_t err = set_smem(kern, smem);
   if (err != hipSuccess) return err;
