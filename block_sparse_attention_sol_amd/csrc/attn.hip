@@ -683,8 +683,13 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(RowStatsArgs a) {
     const float var = pair_sum(vpart) / (float)D;
     const float sigma = sqrtf(fmaxf(var, 0.f));
     const float tau = isinf(a.beta) ? a.beta : fmaf(a.beta, sigma, mu);
+    // sigma = 0 (one key block, q = 0, or identical pooled keys): every proxy of the row equals
+    // mu = tau, so s >= tau keeps every block and the row is dense.  The fused kernel's s and this
+    // mu are rounded along different paths and need not compare equal, so the threshold it reads
+    // says so directly; the exported tau stays mu + beta * sigma.
+    const float tau_sel = (!isinf(a.beta) && var <= 0.f) ? -INFINITY : tau;
     if (valid && h == 0) {
-      a.tau[bh * a.N + row] = tau;
+      a.tau[bh * a.N + row] = tau_sel;
       if (a.mu) a.mu[bh * a.N + row] = mu;
       if (a.sigma) a.sigma[bh * a.N + row] = sigma;
       if (a.tau_out) a.tau_out[bh * a.N + row] = tau;

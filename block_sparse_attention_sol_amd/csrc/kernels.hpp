@@ -24,7 +24,7 @@ struct RowStatsArgs {
   const float* kglob;     // [BH][d]
   int64_t BH, N;
   float beta;
-  float* tau;             // [BH][N] (workspace)
+  float* tau;             // [BH][N] (workspace): selection threshold, -inf where sigma = 0
   float* mu;              // optional outputs
   float* sigma;
   float* tau_out;

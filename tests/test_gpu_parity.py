@@ -142,7 +142,8 @@ def test_sparse_tiny_workload(sol, beta):
 @pytest.mark.parametrize("N,d,block,beta", [(1000, 128, 128, 0.8), (333, 64, 64, 0.3),
                                             (1000, 64, 128, 1.1), (700, 128, 64, 0.6),
                                             (1, 128, 128, 0.5), (129, 64, 64, -0.2),
-                                            (4100, 128, 128, 2.0)])
+                                            (4100, 128, 128, 2.0), (137, 128, 64, -INF),
+                                            (260, 128, 128, INF), (17, 128, 64, 1.0)])
 def test_sparse_ragged(sol, N, d, block, beta):
     """Ragged N: partial last key block, partial last query tile, one-token inputs."""
     _log(f"sparse ragged N={N} d={d} block={block} beta={beta}")
@@ -150,10 +151,29 @@ def test_sparse_ragged(sol, N, d, block, beta):
     _sparse_vs_oracle(sol, q, k, v, beta, block, what=f"ragged N={N}")
 
 
-def test_sparse_batch(sol):
-    _log("sparse B=2 H=3")
-    q, k, v = _qkv(2, 3, 640, 64, seed=11, scale=1.2)
-    _sparse_vs_oracle(sol, q, k, v, 0.4, 64, what="batch")
+@pytest.mark.parametrize("d,block", [(64, 64), (128, 128)])
+def test_sparse_batch(sol, d, block):
+    _log(f"sparse B=2 H=3 d={d}")
+    q, k, v = _qkv(2, 3, 640, d, seed=11, scale=1.2)
+    _sparse_vs_oracle(sol, q, k, v, 0.4, block, what=f"batch d={d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N,beta", [(300, 1.0), (300, -0.5), (40, 2.0)])
+def test_sigma_zero_rows_are_dense(sol, d, N, beta):
+    """Rows whose proxies are all equal (sigma = 0: q = 0, or a single key block when N <= block)
+    keep every block for any finite beta (s = mu = tau), so their output is dense attention."""
+    _log(f"sigma = 0 rows d={d} N={N} beta={beta}")
+    block = 64
+    q, k, v = _qkv(1, 2, N, d, seed=N + d, scale=1.3)
+    zero_rows = [0, 5, N - 1]
+    q[:, :, zero_rows, :] = 0
+    out, dbg = _sparse_vs_oracle(sol, q, k, v, beta, block, what=f"sigma0 d={d} N={N}")
+    M = (N + block - 1) // block
+    mask = oracle.mask_bits(dbg["mask"][0, 0].cpu().numpy().view(np.uint32), M)
+    assert mask[zero_rows].all(), "q = 0 rows must keep every block"
+    if M == 1:
+        assert mask.all(), "with one key block every row keeps it"
 
 
 def test_beta_limits_match_dense_and_pooled(sol):
