@@ -1063,19 +1063,24 @@ __device__ __forceinline__ void exact_stage16(const lds_u8* ktile, const lds_u8*
                                               f32x4 (&o)[D / 16], int lane) {
   constexpr int NT16 = kStage / 16;  // 16-key score tiles per stage
   constexpr int KS = D / 32;         // k steps per tile
+  static_assert(KS == 4, "the address arithmetic below assumes 16 chunks per row");
   const int q = lane & 15, g = lane >> 4;
+  // Swizzled addresses without per-read arithmetic: row q's swizzle f(q) is shared by rows
+  // 16 kt + q, and chunk kk + 4 g = kk ^ 4 g, so the K read (kt, kk) sits at
+  // (q's row offset + ((4 g ^ f(q)) << 4)) ^ (kk << 4), plus kt * 16 rows.
+  const int krel = q * (2 * D) + (((KS * g) ^ swz<D>(q, 0)) << 4);
+  auto kaddr = [&](int kt, int kk) { return ktile + 16 * kt * (2 * D) + (krel ^ (kk << 4)); };
   // Q.K^T, software-pipelined by hand: the operand reads of tile kt + 1 are issued before tile
   // kt's matrix instructions, so two tiles' reads are in flight at most
   f32x4 s[NT16];
   u32x4 kr[2][KS];
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) kr[0][kk] = lds_read16(ktile + tile_off<D>(q, kk + KS * g));
+  for (int kk = 0; kk < KS; ++kk) kr[0][kk] = lds_read16(kaddr(0, kk));
 #pragma unroll
   for (int kt = 0; kt < NT16; ++kt) {
     if (kt + 1 < NT16) {
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-        kr[(kt + 1) & 1][kk] = lds_read16(ktile + tile_off<D>(16 * (kt + 1) + q, kk + KS * g));
+      for (int kk = 0; kk < KS; ++kk) kr[(kt + 1) & 1][kk] = lds_read16(kaddr(kt + 1, kk));
     }
     s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1130,16 +1135,18 @@ __device__ __forceinline__ void exact_stage16(const lds_u8* ktile, const lds_u8*
   // lane q receives column q of those rows.
   const int j = q;
   constexpr int NPV = (NT16 / 2) * (D / 16);
+  // lane j of row g points at key row 4g + j / 4 (+ 32 grp, + 16 for the second read; neither
+  // changes the swizzle) and columns 16 dt + 4 (j % 4): chunk 2 dt + (j % 4) / 2 = 2 dt ^ x, so
+  // the address is the dt = 0 one XOR (dt << 5)
+  const int rr = 4 * g + (j >> 2);
+  const int vrel = rr * (2 * D) + ((((j & 3) >> 1) ^ swz<D>(rr, 0)) << 4) + (j & 1) * 8;
   s16x4 vr[2][2];
   auto read_v = [&](int idx, s16x4 (&dst)[2]) {
     const int grp = idx / (D / 16), dt = idx % (D / 16);
-    const int r1 = 32 * grp + 4 * g + (j >> 2);
-    const int c = 16 * dt + 4 * (j & 3);
-    const int half = ((c >> 2) & 1) * 8;
-    dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(vtile + tile_off<D>(r1, c >> 3) + half));
+    const lds_u8* p = vtile + 32 * grp * (2 * D) + (vrel ^ (dt << 5));
+    dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
     dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(vtile + tile_off<D>(r1 + 16, c >> 3) + half));
+        (__attribute__((address_space(3))) s16x4*)(p + 16 * (2 * D)));
   };
   read_v(0, vr[0]);
 #pragma unroll
@@ -1288,11 +1295,13 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     constexpr int KS = D / 32;
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     u32x4 kr[2][KS];
+    // row qv's swizzle is shared by rows 16 bt + qv, and chunk kk + 4 gv = kk ^ 4 gv (see
+    // exact_stage16)
+    const int krel = qv * (2 * D) + (((KS * gv) ^ swz<D>(qv, 0)) << 4);
     auto read_step = [&](int st, u32x4 (&dst)[KS]) {
-      const lds_u8* tl = base + (st >> 1) * kChunkTile;
+      const lds_u8* tl = base + (st >> 1) * kChunkTile + 16 * (st & 1) * (2 * D);
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-        dst[kk] = lds_read16(tl + tile_off<D>(16 * (st & 1) + qv, kk + KS * gv));
+      for (int kk = 0; kk < KS; ++kk) dst[kk] = lds_read16(tl + (krel ^ (kk << 4)));
     };
     read_step(0, kr[0]);
 #pragma unroll
