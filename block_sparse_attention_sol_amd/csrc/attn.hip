@@ -1433,13 +1433,13 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
       load_rows_share<D, kStage, NT>(vb, r0, a.N, sn, ku, lane_v, base + kTileBytes);
     }
   };
-  // selection words through a buffer resource: scalar word offset, 32-bit lane offset
-  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      rmask, (short)0, (int)((int64_t)W * a.N * 4), 0x00020000);
+  // selection words through a buffer resource over word row wd (N words, at most 16 MB): scalar
+  // base, 32-bit lane offset
   const uint32_t wvoff = (uint32_t)(row * 4);
   auto load_word = [&](int wd) -> uint32_t {
-    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)wd * a.N * 4));
-    return rvalid ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(wrsrc, wvoff, soff, 0) : 0u;
+    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        rmask + (int64_t)wd * a.N, (short)0, (int)(a.N * 4), 0x00020000);
+    return rvalid ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(wrsrc, wvoff, 0, 0) : 0u;
   };
   // The iterator runs one stage ahead of the copies: the stage after next is found after this
   // stage's math, while its last matrix instructions drain.

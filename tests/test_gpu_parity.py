@@ -176,6 +176,35 @@ def test_sigma_zero_rows_are_dense(sol, d, N, beta):
         assert mask.all(), "with one key block every row keeps it"
 
 
+def test_many_key_blocks(sol):
+    """N = 2^21 tokens in 64-key blocks: 32768 key blocks, 1024 selection words per row, so the
+    per-row selection words of one head (8 GB) exceed a 32-bit byte range.  Sampled rows against
+    the oracle; only those rows' words are copied back."""
+    N, d, block, beta = 1 << 21, 128, 64, 3.0
+    _log(f"many key blocks: N={N} d={d} block={block} beta={beta}")
+    q, k, v = _qkv(1, 1, N, d, seed=21, scale=1.0)
+    out, dbg = sol.attn_fwd(q, k, v, beta, block, debug=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([sample_rows(N, 48, seed=3),
+                                     [0, 127, 128, N // 2 + 15, N - 129, N - 1]]))
+    rows_t = torch.from_numpy(rows).cuda()
+    gmask = dbg["mask"][0, 0].index_select(0, rows_t).cpu().numpy().view(np.uint32)
+    got = dbg["out_f32"][0, 0].index_select(0, rows_t).cpu().numpy()
+    gout = out[0, 0].index_select(0, rows_t).float().cpu().numpy()
+    del dbg
+    qh, kh, vh = _np(q[0, 0]), _np(k[0, 0]), _np(v[0, 0])
+    ref = oracle.attn_rows(qh, kh, vh, beta, block, rows=rows)
+    nm, _ = check_mask(gmask, qh, kh, vh, beta, block, rows=rows, ref_mask=ref["mask"])
+    M = (N + block - 1) // block
+    kept = oracle.mask_bits(gmask, M).sum(axis=1)
+    assert kept.min() > 0, "every sampled row keeps some block at this beta"
+    ref_g = oracle.attn_rows(qh, kh, vh, beta, block, rows=rows, mask_override=gmask)
+    ma, mr = assert_close(got, ref_g["out"], "many key blocks (gpu mask)")
+    assert_close_bf16_output(gout, ref["out"], "many key blocks (bf16)")
+    _log(f"many key blocks: {nm} near-tie mask entries, kept blocks per row {kept.min()}..{kept.max()}, "
+         f"max-abs {ma:.3e} mean-rel {mr:.3e}")
+
+
 def test_beta_limits_match_dense_and_pooled(sol):
     """beta = -inf equals the dense kernel; beta = +inf equals pooled-token attention."""
     _log("beta limits")
