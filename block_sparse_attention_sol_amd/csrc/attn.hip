@@ -1385,7 +1385,14 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
   // ---- exact attention over the kept blocks, double-buffered 64-key stages ----
   // Stage iterator over the union, with the set of waves that have math in each stage (bit w:
   // some row of wave w keeps the block).  All values are wave-uniform.
-  int it_w = -1;
+  // The walk over the union starts at block p0 and wraps around.  The i-th tile run on an XCD
+  // starts at i * M / 64 (64 tiles run on an XCD at a time, started in turn): in the steady
+  // state the tiles running together then sweep the same region of keys at the same time, so
+  // the K/V blocks they share are read from HBM once and served from L2 to the others.
+  const int p0 = (int)(((int64_t)(blockIdx.x / 8) * a.M / 64) % a.M);
+  const int w0 = p0 >> 5;
+  const uint32_t low0 = (1u << (p0 & 31)) - 1u;  // blocks of word w0 below p0: visited last
+  int it_k = -1, it_w = -1;
   uint32_t it_u = 0u, it_act = 0u;
   uint32_t it_ww = 0u;  // lane w < kWaves16: wave w's selection word for union word it_w
   int it_j = -1, it_s = kStagesPerBlock;
@@ -1399,9 +1406,12 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
         return true;
       }
       while (it_u == 0u) {
-        if (++it_w >= W) return false;
+        if (++it_k > W) return false;
+        it_w = it_k < W ? (w0 + it_k) % W : w0;
         it_ww = lane < kWaves16 ? wmask[lane * W + it_w] : 0u;
         it_u = union_of_waves(it_ww);
+        if (it_k == 0) it_u &= ~low0;
+        if (it_k == W) it_u &= low0;
       }
       const int b = __builtin_ctz(it_u);
       it_u &= it_u - 1u;
