@@ -1319,12 +1319,6 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     }
     __builtin_amdgcn_sched_group_barrier(kSgMfma, KS, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // the next chunk's copy, issued while the proxy matrix instructions drain (every wave has math
-    // here, so a copy issued at the top of the chunk would hold back the whole workgroup)
-    if (cb + 1 < nchunks) {
-      issue_chunk(cb + 1, b ^ 1);
-      win_next = in_word(cb + 1);
-    }
     // register (bt, i) of lane row g holds block 16 bt + 4 g + i of the chunk
     uint32_t bits = 0u;
     float x[2][4];
@@ -1362,6 +1356,13 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
       if (a.mask_out) a.mask_out[(bh * a.N + row) * W + cb] = word;
     }
     if (g == 0 && word) atomicOr(&wmask[wave * W + cb], word);
+    // the next chunk's copy: after the proxy matrix instructions (every wave has math here, so a
+    // copy issued at the top of the chunk would hold back the whole workgroup) and after this
+    // chunk's selection store (which would otherwise queue behind the copies)
+    if (cb + 1 < nchunks) {
+      issue_chunk(cb + 1, b ^ 1);
+      win_next = in_word(cb + 1);
+    }
     if (!a.drop) {
       cmax = quad_max(cmax);
       raise_max16<D>(cmax, true, mrun, lsum, o);
