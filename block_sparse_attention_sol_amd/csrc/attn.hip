@@ -14,8 +14,10 @@
 //                    mean and covariance of the pooled keys: the mean and population variance of
 //                    the proxy row, exactly, without visiting its M entries.  C q is one bf16
 //                    matrix product per 32 rows over the hi + mid + lo pieces of C (fp32-accurate).
-//                    Writes tau_i = mu_i + beta * sigma_i.
-//   sol_attn_kernel  one workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns
+//                    Writes tau_i = mu_i + beta * sigma_i (-inf for the fused kernel where
+//                    sigma_i = 0: every proxy of such a row equals tau, so it keeps every block).
+//   sol_attn_kernel  (head dimension 64) one workgroup = 4 waves = 128 query rows of one
+//                    (batch, head); each wave owns
 //                    32 rows, one row per lane pair (lanes c and c + 32).  Scores are computed
 //                    transposed, S^T = K Q^T, with Q resident in registers as the B operand, so a
 //                    lane sees its own query's scores.
@@ -29,6 +31,12 @@
 //                    next stage's copy overlapping this stage's math; S^T = K Q^T, rows that did not
 //                    keep the block are masked, online softmax, O^T += V^T P^T with V^T read from
 //                    the row-major V tile by the LDS transpose read (ds_read_b64_tr_b16).
+//   sol_attn16_kernel (head dimension 128) the same stages with eight waves of 16 rows per
+//                    128-row tile on the 16x16x32 matrix instructions: a wave skips a stage when
+//                    none of its 16 rows keeps the block, and two workgroups per CU give four
+//                    waves per SIMD.  Stages are pipelined by hand, idle waves issue the next
+//                    stage's copy, and each tile's walk over its union starts at a point that
+//                    lines up the tiles running together on an XCD.
 //   dense_attn_kernel the exact loop over every key: the reference the speedup is measured against.
 // The proxy map is never written to memory; only the optional debug outputs leave the kernel.
 #include <math.h>
@@ -702,8 +710,9 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(RowStatsArgs a) {
 // ---------------------------------------------------------------------------------------------
 
 // WAVES waves (32 query rows each) share each staged K/V tile: 4 (one 128-row tile, two
-// workgroups per CU) or 8 (two 128-row tiles, one workgroup per CU, every copy feeding twice the
-// rows; d = 128 only, whose 32-row pooled-key chunks split into whole loads for 512 threads).
+// workgroups per CU; launched at d = 64) or 8 (two 128-row tiles, one workgroup per CU, every
+// copy feeding twice the rows; d = 128 only, whose 32-row pooled-key chunks split into whole
+// loads for 512 threads; measured slower and not launched).
 template <int D, int BLK, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void sol_attn_kernel(SparseArgs a) {
   constexpr int NT = 64 * WAVES;       // threads
