@@ -759,6 +759,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void sol_attn_kernel(SparseA
   const int n_last = (int)(a.N - (a.M - 1) * (int64_t)a.block);
   const float l2n_full = log2f((float)a.block);
   const float l2n_last = log2f((float)n_last);
+  // blocks [0, full_end) hold `block` keys each; a partial last block ends the range early
+  const int64_t full_end = a.M - (n_last < a.block ? 1 : 0);
 
   for (int i = t; i < HALVES * W; i += NT) umask[i] = 0u;
 
@@ -806,7 +808,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void sol_attn_kernel(SparseA
     float x[16];
     float cmax = -INFINITY;
     const int nvalid = (int)(a.M - (int64_t)cb * 32);  // blocks of this chunk below M
-    if (nvalid >= 32) {  // wave-uniform: every block of the chunk exists and is full-size
+    if ((int64_t)cb * 32 + 32 <= full_end) {  // wave-uniform: all 32 blocks exist, full-size
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int kj = key_of(v, h);
@@ -1264,6 +1266,8 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
   const int n_last = (int)(a.N - (a.M - 1) * (int64_t)a.block);
   const float l2n_full = log2f((float)a.block);
   const float l2n_last = log2f((float)n_last);
+  // blocks [0, full_end) hold `block` keys each; a partial last block ends the range early
+  const int64_t full_end = a.M - (n_last < a.block ? 1 : 0);
 
   for (int i = t; i < kWaves16 * W; i += NT) wmask[i] = 0u;
 
@@ -1333,7 +1337,7 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     float x[2][4];
     float cmax = -INFINITY;
     const int nvalid = (int)(a.M - (int64_t)cb * 32);  // blocks of this chunk below M
-    if (nvalid >= 32) {  // wave-uniform: every block of the chunk exists and is full-size
+    if ((int64_t)cb * 32 + 32 <= full_end) {  // wave-uniform: all 32 blocks exist, full-size
 #pragma unroll
       for (int bt = 0; bt < 2; ++bt)
 #pragma unroll

@@ -143,7 +143,12 @@ def test_sparse_tiny_workload(sol, beta):
                                             (1000, 64, 128, 1.1), (700, 128, 64, 0.6),
                                             (1, 128, 128, 0.5), (129, 64, 64, -0.2),
                                             (4100, 128, 128, 2.0), (137, 128, 64, -INF),
-                                            (260, 128, 128, INF), (17, 128, 64, 1.0)])
+                                            (260, 128, 128, INF), (17, 128, 64, 1.0),
+                                            # M = 32 pooled blocks (one whole routing chunk) whose
+                                            # last block holds 1 or 2 tokens: its pooled logit
+                                            # carries ln 1 or ln 2, not ln(block)
+                                            (3969, 128, 128, 0.7), (1985, 128, 64, 0.9),
+                                            (1985, 64, 64, 0.4), (3970, 64, 128, 1.0)])
 def test_sparse_ragged(sol, N, d, block, beta):
     """Ragged N: partial last key block, partial last query tile, one-token inputs."""
     _log(f"sparse ragged N={N} d={d} block={block} beta={beta}")
