@@ -68,6 +68,13 @@ __device__ __forceinline__ int swz(int row, int ch) {
     return ch ^ (((row & 3) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1));
   else return ch ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
+// Pooled-key chunk tiles of the 16-row kernel (D = 128, 32 rows): the proxy reads take rows in
+// the order 8 (q / 4) + 4 bt + q % 4 for lane q and block tile bt (so that lane row g's scores are
+// blocks 8g .. 8g + 7), which leaves row bit 2 fixed across the 16 lanes of a read; the swizzle
+// takes row bits 0, 1, 3 and 4, distinct for those 16 rows.
+__device__ __forceinline__ int swz_pk(int row, int ch) {
+  return ch ^ (((row & 3) << 2) | ((row >> 3) & 3));
+}
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int ch) {  // byte offset of a 16-byte chunk
   return row * (2 * D) + (swz<D>(row, ch) << 4);
@@ -118,8 +125,10 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
 // Per-lane byte offsets, within a ROWS-row tile of a bf16 matrix with rows of D contiguous
 // elements sn elements apart, of the 16 bytes each lane copies so that the LDS tile comes out
 // swizzled (see load_tile).
-template <int D, int ROWS, int NT = kThreads>
+// PK: the pooled-key tile swizzle (swz_pk) instead of swz.
+template <int D, int ROWS, int NT = kThreads, bool PK = false>
 struct TileOffsets {
+  static_assert(!PK || D == 128, "the pooled-key swizzle covers 16 chunks per row");
   uint32_t v[tile_loads<D, ROWS, NT>()];
   __device__ __forceinline__ explicit TileOffsets(int64_t sn, int tid = (int)threadIdx.x) {
     constexpr int kChunks = D / 8;
@@ -127,7 +136,8 @@ struct TileOffsets {
     for (int i = 0; i < tile_loads<D, ROWS, NT>(); ++i) {
       const int p = i * NT + tid;
       const int row = p / kChunks;
-      v[i] = (uint32_t)(row * sn * 2 + swz<D>(row, p % kChunks) * 16);
+      const int ch = PK ? swz_pk(row, p % kChunks) : swz<D>(row, p % kChunks);
+      v[i] = (uint32_t)(row * sn * 2 + ch * 16);
     }
   }
 };
@@ -159,9 +169,9 @@ __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t soff
       : "memory");
 }
 
-template <int D, int ROWS, int NT = kThreads>
+template <int D, int ROWS, int NT = kThreads, bool PK = false>
 __device__ __forceinline__ void load_tile_buf(i32x4_t rsrc, uint32_t soff,
-                                              const TileOffsets<D, ROWS, NT>& off, lds_u8* tile) {
+                                              const TileOffsets<D, ROWS, NT, PK>& off, lds_u8* tile) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int i = 0; i < tile_loads<D, ROWS, NT>(); ++i)
@@ -172,10 +182,10 @@ __device__ __forceinline__ void load_tile_buf(i32x4_t rsrc, uint32_t soff,
 // pieces, padded to Mp rows), copied as load_tile does but without the compiler's LDS-DMA builtin
 // (see load_tile_buf): a builtin copy in flight makes the compiler wait for every outstanding
 // memory operation before the next LDS write, which stalls the routing sweep once per chunk.
-template <int D, int ROWS, int NT = kThreads>
+template <int D, int ROWS, int NT = kThreads, bool PK = false>
 __device__ __forceinline__ void load_dense_rows(const uint16_t* src, int64_t row0,
-                                                const TileOffsets<D, ROWS, NT>& off, lds_u8* tile) {
-  load_tile_buf<D, ROWS, NT>(make_rsrc(src + row0 * D, ROWS * D * 2), 0u, off, tile);
+                                                const TileOffsets<D, ROWS, NT, PK>& off, lds_u8* tile) {
+  load_tile_buf<D, ROWS, NT, PK>(make_rsrc(src + row0 * D, ROWS * D * 2), 0u, off, tile);
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -1025,23 +1035,18 @@ __device__ __forceinline__ bf16x8 p_operand16(const uint32_t (&pk)[4]) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// O^T[dt] += Vbar^T P^T for the 32 pooled blocks of a routing chunk: the A operand of lane (g, q)
-// is row 16 dt + q of the Vbar^T chunk tile at blocks 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3,
-// two 8-byte reads.
+// O^T[dt] += Vbar^T P^T for the 32 pooled blocks of a routing chunk.  Lane row g holds the
+// probabilities of blocks 8g .. 8g + 7 (the proxy reads take the pooled-key rows in that order), so
+// the A operand of lane (g, q) is row 16 dt + q of the Vbar^T chunk tile at blocks 8g .. 8g + 7:
+// one 16-byte chunk, whose swizzle (vbt_off) is the same for every dt.
 template <int D>
 __device__ __forceinline__ void pv_pooled16(const lds_u8* vt, const bf16x8& b, f32x4 (&o)[D / 16],
                                             int lane) {
   const int q = lane & 15, g = lane >> 4;
-  const int off = 8 * (g & 1);
+  const lds_u8* base = vt + vbt_off<D>(q, g);
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
-    const int row = 16 * dt + q;
-    const u32x2 x0 = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
-        vt + vbt_off<D>(row, g >> 1) + off);
-    const u32x2 x1 = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
-        vt + vbt_off<D>(row, 2 + (g >> 1)) + off);
-    u32x4 raw;
-    raw[0] = x0[0]; raw[1] = x0[1]; raw[2] = x1[0]; raw[3] = x1[1];
+    const u32x4 raw = lds_read16(base + dt * 16 * 64);
     o[dt] = mfma16(__builtin_bit_cast(bf16x8, raw), b, o[dt]);
   }
 }
@@ -1281,7 +1286,7 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
   float mrun = -1e30f;  // running max, log2 domain
   float lsum = 0.f;
   const int nchunks = (int)(a.Mp / 32);
-  const TileOffsets<D, 32, NT> coff(D);
+  const TileOffsets<D, 32, NT, true> coff(D);
   const VbtOffsets<D, NT> voff(a.Mp);
   auto issue_chunk = [&](int cb, int b) {
     lds_u8* base = smem + b * kRouteBuf;
@@ -1308,11 +1313,13 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     constexpr int KS = D / 32;
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     u32x4 kr[2][KS];
-    // row qv's swizzle is shared by rows 16 bt + qv, and chunk kk + 4 gv = kk ^ 4 gv (see
-    // exact_stage16)
-    const int krel = qv * (2 * D) + (((KS * gv) ^ swz<D>(qv, 0)) << 4);
+    // lane qv reads pooled-key row 8 (qv / 4) + 4 bt + qv % 4 (block tile bt = st & 1), so that the
+    // result registers (bt, i) of lane row g are block 8g + 4bt + i; that row's swizzle is the same
+    // for both bt, and chunk kk + 4 gv = kk ^ 4 gv (see exact_stage16)
+    const int prow = 8 * (qv >> 2) + (qv & 3);
+    const int krel = prow * (2 * D) + (swz_pk(prow, KS * gv) << 4);
     auto read_step = [&](int st, u32x4 (&dst)[KS]) {
-      const lds_u8* tl = base + (st >> 1) * kChunkTile + 16 * (st & 1) * (2 * D);
+      const lds_u8* tl = base + (st >> 1) * kChunkTile + 4 * (st & 1) * (2 * D);
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) dst[kk] = lds_read16(tl + (krel ^ (kk << 4)));
     };
@@ -1332,43 +1339,52 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     }
     __builtin_amdgcn_sched_group_barrier(kSgMfma, KS, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // register (bt, i) of lane row g holds block 16 bt + 4 g + i of the chunk
-    uint32_t bits = 0u;
+    // register (bt, i) of lane row g holds block 8g + e of the chunk, e = 4bt + i; lb collects the
+    // lane row's 8 selection bits at bits e, and the row's word has them at 8g + e
+    uint32_t lb = 0u;
     float x[2][4];
-    float cmax = -INFINITY;
-    const int nvalid = (int)(a.M - (int64_t)cb * 32);  // blocks of this chunk below M
     if ((int64_t)cb * 32 + 32 <= full_end) {  // wave-uniform: all 32 blocks exist, full-size
 #pragma unroll
       for (int bt = 0; bt < 2; ++bt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int kj = 16 * bt + 4 * g + i;
-          const bool sel = has_in ? ((win >> kj) & 1u) != 0u : acc[bt][i] >= tau_raw;
-          bits |= (sel ? 1u : 0u) << kj;
+          const bool sel = acc[bt][i] >= tau_raw;  // tau is +inf with a caller's selection
+          lb |= sel ? (1u << (4 * bt + i)) : 0u;
           x[bt][i] = sel ? -INFINITY : fmaf(acc[bt][i], sl2, l2n_full);
-          cmax = fmaxf(cmax, x[bt][i]);
         }
+      if (has_in) {  // wave-uniform: the caller's words decide
+        lb = (win >> (8 * g)) & 0xffu;
+#pragma unroll
+        for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if ((lb >> (4 * bt + i)) & 1u) x[bt][i] = -INFINITY;
+      }
     } else {
+      const int nvalid = (int)(a.M - (int64_t)cb * 32);  // blocks of this chunk below M
 #pragma unroll
       for (int bt = 0; bt < 2; ++bt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int kj = 16 * bt + 4 * g + i;
+          const int kj = 8 * g + 4 * bt + i;
           const bool valid = kj < nvalid;
           const bool sel = valid & (has_in ? ((win >> kj) & 1u) != 0u : acc[bt][i] >= tau_raw);
-          bits |= (sel ? 1u : 0u) << kj;
+          lb |= (sel ? 1u : 0u) << (4 * bt + i);
           x[bt][i] = (valid & !sel)
                          ? fmaf(acc[bt][i], sl2, kj == nvalid - 1 ? l2n_last : l2n_full)
                          : -INFINITY;
-          cmax = fmaxf(cmax, x[bt][i]);
         }
     }
-    const uint32_t word = quad_or(bits);
+    float cmax = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+    const uint32_t word = quad_or(lb << (8 * g));
     if (g == 0 && rvalid) {
       rmask[(int64_t)cb * a.N + row] = word;
       if (a.mask_out) a.mask_out[(bh * a.N + row) * W + cb] = word;
     }
-    if (g == 0 && word) atomicOr(&wmask[wave * W + cb], word);
+    // the wave's union: each wave owns its word, so one lane stores the OR of its 16 rows
+    const uint32_t wword = row16_or(word);
+    if (lane == 0) wmask[wave * W + cb] = wword;
     // the next chunk's copy: after the proxy matrix instructions (every wave has math here, so a
     // copy issued at the top of the chunk would hold back the whole workgroup) and after this
     // chunk's selection store (which would otherwise queue behind the copies)

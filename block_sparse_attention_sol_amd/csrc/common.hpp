@@ -122,5 +122,14 @@ __device__ __forceinline__ uint32_t quad_or(uint32_t x) {
   row_pair_values(x, a, b);
   return pair_or(a | b);
 }
+// OR over the 16 lanes of each 16-lane row, every lane of the row receiving the value (DPP moves:
+// swap neighbours, swap neighbour pairs, mirror within 8 lanes, mirror within 16; all lanes active).
+__device__ __forceinline__ uint32_t row16_or(uint32_t x) {
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false);  // row_mirror
+  return x;
+}
 
 }  // namespace solattn
