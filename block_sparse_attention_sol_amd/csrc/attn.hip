@@ -52,7 +52,13 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kStage = 64;  // keys per pipeline stage
-constexpr int kRowStatsTiles = 16;  // query tiles per row-statistics workgroup (C staged once)
+// Row statistics: eight waves of 32 rows share the staged covariance pieces (two waves per SIMD
+// hide each other's latency; the pieces' 96 KB of LDS at d = 128 allow one workgroup per CU),
+// over kRowStatsPasses passes of 256 rows.
+constexpr int kRowStatsWaves = 8;
+constexpr int kRowStatsThreads = 64 * kRowStatsWaves;
+constexpr int kRowStatsRows = 32 * kRowStatsWaves;  // rows per pass
+constexpr int kRowStatsPasses = 8;
 
 // ---------------------------------------------------------------------------------------------
 // LDS tiles: row-major [rows][D] bf16, 16-byte chunks XOR-swizzled per row.  The swizzle makes
@@ -630,63 +636,100 @@ __device__ __forceinline__ bool work_item(int64_t total, int64_t& w) {
 // ---------------------------------------------------------------------------------------------
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void rowstats_kernel(RowStatsArgs a) {
+__global__ __launch_bounds__(kRowStatsThreads) void rowstats_kernel(RowStatsArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   lds_u8* smem = (lds_u8*)smem_raw;
-  const int64_t ntiles = (a.N + kQTile - 1) / kQTile;
-  const int64_t groups = (ntiles + kRowStatsTiles - 1) / kRowStatsTiles;
+  constexpr int64_t kGroupRows = (int64_t)kRowStatsRows * kRowStatsPasses;
+  const int64_t groups = (a.N + kGroupRows - 1) / kGroupRows;
   const int64_t bh = blockIdx.x / groups;
   const int64_t grp = blockIdx.x % groups;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane & 31, h = lane >> 5;
+  const int lane = threadIdx.x & 63, c = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
 
-  // C pieces -> LDS, smallest first: tile p holds piece lo (p = 0), mid (1), hi (2)
+  // C pieces -> LDS, smallest first: tile p holds piece lo (p = 0), mid (1), hi (2); then kglob
   const uint16_t* cbase = a.cp + bh * D * D;
   const int64_t piece = a.BH * D * D;
 #pragma unroll
   for (int p = 0; p < 3; ++p)
-    load_tile<D, D>(cbase + (2 - p) * piece, 0, D, smem + p * D * D * 2);
+    load_tile<D, D, kRowStatsThreads>(cbase + (2 - p) * piece, 0, D, smem + p * D * D * 2);
+  float* kgl = (float*)(smem_raw + 3 * D * D * 2);
+  for (int i = threadIdx.x; i < D; i += kRowStatsThreads) kgl[i] = a.kglob[bh * D + i];
   wait_vmcnt<0>();
   __syncthreads();
 
   const float inv_sqrt_d = 1.0f / sqrtf((float)D);
-  const float* kg = a.kglob + bh * D;
-  for (int tt = 0; tt < kRowStatsTiles; ++tt) {
-    const int64_t tile = grp * kRowStatsTiles + tt;
-    if (tile >= ntiles) break;
-    const int64_t row = tile * kQTile + wave * 32 + c;
+  // C operand of (piece p, k step kk, row tile ab): row 32 ab + c, chunk 2 kk + h.  The row swizzle
+  // reads row bits below 5 only, so ab and p add whole tiles and kk flips chunk bits:
+  // offset = p D D 2 + ab 32 2D + (crel ^ (kk << 5)).
+  const int crel = c * (2 * D) + (swz<D>(c, h) << 4);
+  const uint16_t* qhead = a.q + a.qs.base(bh);
+  for (int pp = 0; pp < kRowStatsPasses; ++pp) {
+    const int64_t r0 = grp * kGroupRows + (int64_t)pp * kRowStatsRows;
+    if (r0 >= a.N) break;
+    const int64_t row0w = r0 + wave * 32;  // this wave's first row
+    const int64_t row = row0w + c;
     const bool valid = row < a.N;
-    const uint16_t* qrow = a.q + a.qs.base(bh) + row * a.qs.sn;
+    // the wave's rows through a buffer resource that ends after its last valid row: rows past N
+    // read as zeros without a branch per load
+    const int64_t nrows = a.N - row0w < 32 ? a.N - row0w : 32;
+    const uint32_t bytes = nrows > 0 ? (uint32_t)((nrows - 1) * a.qs.sn * 2 + D * 2) : 0u;
+    const __amdgpu_buffer_rsrc_t qrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(qhead + row0w * a.qs.sn), (short)0, (int)bytes,
+                                          0x00020000);
+    const uint32_t qoff = (uint32_t)(c * a.qs.sn * 2);
     bf16x8 qf[D / 16];
-    load_q<D>(qrow, valid, qf);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qf[kk] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff + (16 * kk + 8 * h) * 2, 0, 0));
     // query values in the layout of C q's rows (a = 32 ab + 8 g + 4 h + 0..3)
     u32x2 qa[D / 32][4];
 #pragma unroll
     for (int ab = 0; ab < D / 32; ++ab)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 qq = {0u, 0u};
-        if (valid) qq = *reinterpret_cast<const u32x2*>(qrow + 32 * ab + 8 * g + 4 * h);
-        qa[ab][g] = qq;
-      }
+      for (int g = 0; g < 4; ++g)
+        qa[ab][g] = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(qrs, qoff + (32 * ab + 8 * g + 4 * h) * 2, 0, 0));
+    // all of the pass's loads are issued here, ahead of the matrix work that hides their latency
+    __builtin_amdgcn_sched_barrier(0);
     float mpart = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const float4 k0 = *reinterpret_cast<const float4*>(kgl + 16 * kk + 8 * h);
+      const float4 k1 = *reinterpret_cast<const float4*>(kgl + 16 * kk + 8 * h + 4);
+      const float kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) mpart = fmaf((float)qf[kk][e], kg[16 * kk + 8 * h + e], mpart);
+      for (int e = 0; e < 8; ++e) mpart = fmaf((float)qf[kk][e], kv[e], mpart);
+    }
     // y[ab][v] = (C q)[32 ab + 8 (v/4) + 4 h + v%4]: D/32 independent accumulation chains,
-    // pieces smallest first
+    // pieces smallest first; the operand reads of step s + 1 are issued before step s's matrix
+    // instructions
+    constexpr int S = 3 * (D / 16);
     f32x16 y[D / 32];
 #pragma unroll
     for (int ab = 0; ab < D / 32; ++ab) y[ab] = f32x16{};
+    u32x4 ra[2][D / 32];
+    auto read_step = [&](int s, u32x4 (&dst)[D / 32]) {
+      const lds_u8* base = smem + (s / (D / 16)) * D * D * 2 + (crel ^ ((s % (D / 16)) << 5));
 #pragma unroll
-    for (int p = 0; p < 3; ++p)
+      for (int ab = 0; ab < D / 32; ++ab) dst[ab] = lds_read16(base + ab * 32 * 2 * D);
+    };
+    read_step(0, ra[0]);
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
+    for (int s = 0; s < S; ++s) {
+      if (s + 1 < S) read_step(s + 1, ra[(s + 1) & 1]);
 #pragma unroll
-        for (int ab = 0; ab < D / 32; ++ab) {
-          const u32x4 raw = lds_read16(smem + p * D * D * 2 + tile_off<D>(32 * ab + c, 2 * kk + h));
-          y[ab] = mfma32(__builtin_bit_cast(bf16x8, raw), qf[kk], y[ab]);
-        }
+      for (int ab = 0; ab < D / 32; ++ab)
+        y[ab] = mfma32(__builtin_bit_cast(bf16x8, ra[s & 1][ab]), qf[s % (D / 16)], y[ab]);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, D / 32, 0);
+#pragma unroll
+    for (int s = 0; s + 1 < S; ++s) {
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, D / 32, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, D / 32, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, D / 32, 0);
+    __builtin_amdgcn_sched_barrier(0);
     float vpart = 0.f;
 #pragma unroll
     for (int ab = 0; ab < D / 32; ++ab)
@@ -1796,13 +1839,13 @@ hipError_t launch_sparse(int d, const SparseArgs& a, hipStream_t stream) {
 
 template <int D>
 static hipError_t launch_rowstats_t(const RowStatsArgs& a, hipStream_t stream) {
-  const size_t smem = (size_t)3 * D * D * 2;
+  const size_t smem = (size_t)3 * D * D * 2 + D * sizeof(float);
   auto kern = rowstats_kernel<D>;
   hipError_t err = set_smem(kern, smem);
   if (err != hipSuccess) return err;
-  const int64_t ntiles = (a.N + kQTile - 1) / kQTile;
-  const int64_t groups = (ntiles + kRowStatsTiles - 1) / kRowStatsTiles;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(a.BH * groups)), dim3(kThreads), smem, stream, a);
+  constexpr int64_t kGroupRows = (int64_t)kRowStatsRows * kRowStatsPasses;
+  const int64_t groups = (a.N + kGroupRows - 1) / kGroupRows;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(a.BH * groups)), dim3(kRowStatsThreads), smem, stream, a);
   return hipGetLastError();
 }
 
