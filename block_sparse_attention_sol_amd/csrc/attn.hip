@@ -34,9 +34,12 @@
 //   sol_attn16_kernel (head dimension 128) the same stages with eight waves of 16 rows per
 //                    128-row tile on the 16x16x32 matrix instructions: a wave skips a stage when
 //                    none of its 16 rows keeps the block, and two workgroups per CU give four
-//                    waves per SIMD.  Stages are pipelined by hand, idle waves issue the next
-//                    stage's copy, and each tile's walk over its union starts at a point that
-//                    lines up the tiles running together on an XCD.
+//                    waves per SIMD.  In the pooled sweep each lane row's proxies are 8
+//                    consecutive blocks (selection bits by constant shifts, one 16-byte operand
+//                    read per pooled product) and a wave's union word is one DPP OR and store.
+//                    Stages are pipelined by hand, idle waves issue the next stage's copy, and
+//                    each tile's walk over its union starts at a point that lines up the tiles
+//                    running together on an XCD.
 //   dense_attn_kernel the exact loop over every key: the reference the speedup is measured against.
 // The proxy map is never written to memory; only the optional debug outputs leave the kernel.
 #include <math.h>
