@@ -227,13 +227,26 @@ __device__ __forceinline__ void load_rows(const uint16_t* base, int64_t r0, int6
 template <int D, int ROWS, int NT>
 __device__ __forceinline__ void load_rows_share(const uint16_t* base, int64_t r0, int64_t limit,
                                                 int64_t sn, int k, int lane, lds_u8* tile) {
+  constexpr int kChunks = D / 8;
+  static_assert(64 % kChunks == 0 && NT % kChunks == 0, "a wave's slots cover whole rows");
   const int64_t rest = (limit - r0 - 1) * sn * 2 + D * 2;
   const uint32_t bytes = (uint32_t)(rest < 0xffffffffll ? rest : 0xffffffffll);
   const i32x4_t rsrc = make_rsrc(base + r0 * sn, bytes);
-  const TileOffsets<D, ROWS, NT> off(sn, k * 64 + lane);
+  // The offsets TileOffsets would give, split into a wave-uniform and a per-lane part: slot
+  // i NT + 64 k + lane holds row rs + rl (rs = (i NT + 64 k) / kChunks, a multiple of
+  // 64 / kChunks, and rl = lane / kChunks < 64 / kChunks) and logical chunk
+  // (lane % kChunks) ^ f(rs + rl).  The swizzle f only permutes row bits, so
+  // f(rs + rl) = f(rs) ^ f(rl).
+  const uint32_t sn2 = (uint32_t)(sn * 2);
+  const int rl = lane / kChunks;
+  const uint32_t lane_row = (uint32_t)rl * sn2;
+  const int cl = swz<D>(rl, lane % kChunks);
 #pragma unroll
-  for (int i = 0; i < tile_loads<D, ROWS, NT>(); ++i)
-    dma16(rsrc, off.v[i], 0u, tile + (i * NT + k * 64) * 16);
+  for (int i = 0; i < tile_loads<D, ROWS, NT>(); ++i) {
+    const int rs = (i * NT + 64 * k) / kChunks;  // wave-uniform
+    const uint32_t voff = (uint32_t)rs * sn2 + lane_row + ((uint32_t)(cl ^ swz<D>(rs, 0)) << 4);
+    dma16(rsrc, voff, 0u, tile + (i * NT + k * 64) * 16);
+  }
 }
 
 __device__ __forceinline__ void bar() {
@@ -769,8 +782,10 @@ __global__ __launch_bounds__(kRowStatsThreads) void rowstats_kernel(RowStatsArgs
 // workgroups per CU; launched at d = 64) or 8 (two 128-row tiles, one workgroup per CU, every
 // copy feeding twice the rows; d = 128 only, whose 32-row pooled-key chunks split into whole
 // loads for 512 threads; measured slower and not launched).
+// Four waves: at most 168 VGPRs, so that three workgroups fit a CU (their LDS does, 33 KB each at
+// d = 64); with 178 only two did, and LTX's fused pass ran 10-18% slower.
 template <int D, int BLK, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void sol_attn_kernel(SparseArgs a) {
+__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 3 : 8 / WAVES) void sol_attn_kernel(SparseArgs a) {
   constexpr int NT = 64 * WAVES;       // threads
   constexpr int QT = 32 * WAVES;       // query rows per workgroup
   constexpr int HALVES = WAVES / 4;    // 128-row tiles per workgroup
