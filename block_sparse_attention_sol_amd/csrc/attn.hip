@@ -163,19 +163,16 @@ struct TileOffsets {
 // are consumed at issue, and the callers order the LDS traffic themselves: wait_vmcnt before the
 // barrier that publishes a tile, and a barrier before a buffer is refilled.
 // One copy of 16 bytes per lane from the buffer `rsrc` (at byte voff + soff) to LDS; lane l lands
-// at dst + 16 l, dst wave-uniform.  The LDS pointer itself is an operand, so the compiler knows
-// this statement writes there; m0 (the LDS destination base of the copy) is saved and restored
-// around it.
+// at dst + 16 l, dst wave-uniform.  The LDS destination base goes in m0 as an operand bound to
+// that register, so the compiler sets m0 itself (one scalar move; it knows m0's value afterwards)
+// and knows this statement writes LDS.  These copies sit in every stage's scalar-bound
+// bookkeeping, where a save and restore of m0 around each would cost two more scalar
+// instructions per copy.
 __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t soff, lds_u8* dst) {
-  uint32_t saved;
-  __asm__ __volatile__(
-      "s_mov_b32 %[saved], m0\n\t"
-      "s_mov_b32 m0, %[m0]\n\t"
-      "buffer_load_dwordx4 %[voff], %[rsrc], %[soff] offen lds\n\t"
-      "s_mov_b32 m0, %[saved]"
-      : [saved] "=&s"(saved)
-      : [m0] "s"(dst), [voff] "v"(voff), [rsrc] "s"(rsrc), [soff] "s"(soff)
-      : "memory");
+  __asm__ __volatile__("buffer_load_dwordx4 %[voff], %[rsrc], %[soff] offen lds"
+                       :
+                       : "{m0}"(dst), [voff] "v"(voff), [rsrc] "s"(rsrc), [soff] "s"(soff)
+                       : "memory");
 }
 
 template <int D, int ROWS, int NT = kThreads, bool PK = false>
@@ -217,27 +214,19 @@ __device__ __forceinline__ void load_rows(const uint16_t* base, int64_t r0, int6
   load_tile_buf<D, ROWS, NT>(make_rsrc(base + r0 * sn, bytes), 0u, off, tile);
 }
 
-// Workgroup barrier without the memory fence of __syncthreads: the pipelined loops order their
-// LDS traffic themselves (explicit vmcnt waits for the LDS-bound copies; LDS reads are consumed
-// before the barrier), so the fence's wait for every outstanding load -- including the next
-// stage's prefetch -- is not wanted.  The empty asm statements keep the compiler from moving
-// memory accesses across it.
 // Share k of the copy load_rows makes of rows [r0, r0 + ROWS) (the loads lane l of wave k issues
-// there), issued by the calling wave instead; k is wave-uniform.
+// there), issued by the calling wave instead; k is wave-uniform.  rsrc starts at row r0 and ends
+// after the head's last valid row (load_rows' range); sn2 is the row stride in bytes.
 template <int D, int ROWS, int NT>
-__device__ __forceinline__ void load_rows_share(const uint16_t* base, int64_t r0, int64_t limit,
-                                                int64_t sn, int k, int lane, lds_u8* tile) {
+__device__ __forceinline__ void copy_share(i32x4_t rsrc, uint32_t sn2, int k, int lane,
+                                           lds_u8* tile) {
   constexpr int kChunks = D / 8;
   static_assert(64 % kChunks == 0 && NT % kChunks == 0, "a wave's slots cover whole rows");
-  const int64_t rest = (limit - r0 - 1) * sn * 2 + D * 2;
-  const uint32_t bytes = (uint32_t)(rest < 0xffffffffll ? rest : 0xffffffffll);
-  const i32x4_t rsrc = make_rsrc(base + r0 * sn, bytes);
   // The offsets TileOffsets would give, split into a wave-uniform and a per-lane part: slot
   // i NT + 64 k + lane holds row rs + rl (rs = (i NT + 64 k) / kChunks, a multiple of
   // 64 / kChunks, and rl = lane / kChunks < 64 / kChunks) and logical chunk
   // (lane % kChunks) ^ f(rs + rl).  The swizzle f only permutes row bits, so
   // f(rs + rl) = f(rs) ^ f(rl).
-  const uint32_t sn2 = (uint32_t)(sn * 2);
   const int rl = lane / kChunks;
   const uint32_t lane_row = (uint32_t)rl * sn2;
   const int cl = swz<D>(rl, lane % kChunks);
@@ -249,6 +238,11 @@ __device__ __forceinline__ void load_rows_share(const uint16_t* base, int64_t r0
   }
 }
 
+// Workgroup barrier without the memory fence of __syncthreads: the pipelined loops order their
+// LDS traffic themselves (explicit vmcnt waits for the LDS-bound copies; LDS reads are consumed
+// before the barrier), so the fence's wait for every outstanding load -- including the next
+// stage's prefetch -- is not wanted.  The empty asm statements keep the compiler from moving
+// memory accesses across it.
 __device__ __forceinline__ void bar() {
   __asm__ __volatile__("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -1515,23 +1509,32 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
   // has none, the idle waves issue the whole copy between them (wave share k to the (k mod
   // #idle)-th idle wave), so that the waves that compute do not queue behind the copy's issue.
   // Copy offsets are recomputed per stage (see fresh_lane).
+  // The scalar work here runs in every wave right after each stage's barrier, through the CU's
+  // one scalar unit, so a computing wave leaves before any of it, and the issuing waves make one
+  // 64-bit product per stage (the head's end offset is fixed per tile).
+  const int64_t end_bytes = (a.N - 1) * sn * 2 + D * 2;  // head start to the end of its last row
+  const uint32_t sn2 = (uint32_t)(sn * 2);
   auto issue = [&](int j, int s, int buf, uint32_t act) {
-    const int64_t r0 = (int64_t)j * BLK + s * kStage;
-    lds_u8* base = smem + buf * kStageBytes;
     const uint32_t idle = ~act & ((1u << kWaves16) - 1u);
+    if (idle != 0u && !((idle >> wave) & 1u)) return;
+    const int64_t roff = ((int64_t)j * BLK + s * kStage) * sn;  // first row, in elements
+    const int64_t rest = end_bytes - 2 * roff;
+    const uint32_t bytes = (uint32_t)(rest < 0xffffffffll ? rest : 0xffffffffll);
+    const i32x4_t krs = make_rsrc(kb + roff, bytes);
+    const i32x4_t vrs = make_rsrc(vb + roff, bytes);
+    lds_u8* base = smem + buf * kStageBytes;
     const int lane_v = fresh_lane();
     if (idle == 0u) {
-      load_rows_share<D, kStage, NT>(kb, r0, a.N, sn, wave, lane_v, base);
-      load_rows_share<D, kStage, NT>(vb, r0, a.N, sn, wave, lane_v, base + kTileBytes);
+      copy_share<D, kStage, NT>(krs, sn2, wave, lane_v, base);
+      copy_share<D, kStage, NT>(vrs, sn2, wave, lane_v, base + kTileBytes);
       return;
     }
-    if (!((idle >> wave) & 1u)) return;
     const int nidle = __builtin_popcount(idle);
     const int rank = __builtin_popcount(idle & ((1u << wave) - 1u));
     for (int k = rank; k < kWaves16; k += nidle) {
       const int ku = __builtin_amdgcn_readfirstlane(k);
-      load_rows_share<D, kStage, NT>(kb, r0, a.N, sn, ku, lane_v, base);
-      load_rows_share<D, kStage, NT>(vb, r0, a.N, sn, ku, lane_v, base + kTileBytes);
+      copy_share<D, kStage, NT>(krs, sn2, ku, lane_v, base);
+      copy_share<D, kStage, NT>(vrs, sn2, ku, lane_v, base + kTileBytes);
     }
   };
   // selection words through a buffer resource over word row wd (N words, at most 16 MB): scalar
