@@ -1034,11 +1034,14 @@ constexpr int kWaves16 = 8;
 constexpr int kThreads16 = 64 * kWaves16;
 
 // OR over lanes 0 .. kWaves16 - 1 of x (the other lanes hold 0), returned in every lane as a
-// wave-uniform value: three butterfly steps within the first 8 lanes, then lane 0's result.
+// wave-uniform value: three DPP steps within each 8-lane group (swap neighbours, swap pairs,
+// mirror the 8; all lanes active), then lane 0's result.  DPP moves are plain vector operations,
+// where cross-lane shuffles would be three dependent LDS-unit round trips.
+static_assert(kWaves16 == 8, "one 8-lane DPP group");
 __device__ __forceinline__ uint32_t union_of_waves(uint32_t x) {
-  x |= (uint32_t)__shfl_xor((int)x, 1);
-  x |= (uint32_t)__shfl_xor((int)x, 2);
-  x |= (uint32_t)__shfl_xor((int)x, 4);
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false);  // row_half_mirror
   return __builtin_amdgcn_readfirstlane(x);
 }
 
@@ -1492,7 +1495,7 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
       }
       while (it_u == 0u) {
         if (++it_k > W) return false;
-        it_w = it_k < W ? (w0 + it_k) % W : w0;
+        it_w = it_k < W ? (w0 + it_k < W ? w0 + it_k : w0 + it_k - W) : w0;  // (w0 + it_k) mod W
         it_ww = lane < kWaves16 ? wmask[lane * W + it_w] : 0u;
         it_u = union_of_waves(it_ww);
         if (it_k == 0) it_u &= ~low0;
