@@ -1509,9 +1509,10 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     }
   };
   // The next stage's copy, issued during a stage whose waves with math are `act`: when some wave
-  // has none, the idle waves issue the whole copy between them (wave share k to the (k mod
-  // #idle)-th idle wave), so that the waves that compute do not queue behind the copy's issue.
-  // Copy offsets are recomputed per stage (see fresh_lane).
+  // has none, the lowest such wave issues the whole copy, so that the waves that compute do not
+  // queue behind the copy's issue.  One issuing wave pays the copy's scalar set-up once; spread
+  // over all idle waves, the set-up ran in each of them through the CU's one scalar unit (3%
+  // slower at Wan).  Copy offsets are recomputed per stage (see fresh_lane).
   // The scalar work here runs in every wave right after each stage's barrier, through the CU's
   // one scalar unit, so a computing wave leaves before any of it, and the issuing waves make one
   // 64-bit product per stage (the head's end offset is fixed per tile).
@@ -1519,7 +1520,7 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
   const uint32_t sn2 = (uint32_t)(sn * 2);
   auto issue = [&](int j, int s, int buf, uint32_t act) {
     const uint32_t idle = ~act & ((1u << kWaves16) - 1u);
-    if (idle != 0u && !((idle >> wave) & 1u)) return;
+    if (idle != 0u && wave != __builtin_ctz(idle)) return;
     const int64_t roff = ((int64_t)j * BLK + s * kStage) * sn;  // first row, in elements
     const int64_t rest = end_bytes - 2 * roff;
     const uint32_t bytes = (uint32_t)(rest < 0xffffffffll ? rest : 0xffffffffll);
@@ -1532,12 +1533,9 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
       copy_share<D, kStage, NT>(vrs, sn2, wave, lane_v, base + kTileBytes);
       return;
     }
-    const int nidle = __builtin_popcount(idle);
-    const int rank = __builtin_popcount(idle & ((1u << wave) - 1u));
-    for (int k = rank; k < kWaves16; k += nidle) {
-      const int ku = __builtin_amdgcn_readfirstlane(k);
-      copy_share<D, kStage, NT>(krs, sn2, ku, lane_v, base);
-      copy_share<D, kStage, NT>(vrs, sn2, ku, lane_v, base + kTileBytes);
+    for (int k = 0; k < kWaves16; ++k) {
+      copy_share<D, kStage, NT>(krs, sn2, k, lane_v, base);
+      copy_share<D, kStage, NT>(vrs, sn2, k, lane_v, base + kTileBytes);
     }
   };
   // selection words through a buffer resource over word row wd (N words, at most 16 MB): scalar
