@@ -200,6 +200,8 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+// s_waitcnt lgkmcnt(0) alone (gfx9 encoding: vmcnt and expcnt left at their maxima).
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
 
 // Rows [r0, r0 + ROWS) of a row-strided bf16 matrix (row r at base + r * sn, rows below `limit`)
 // into an LDS tile; rows at or beyond `limit` read as zeros (the buffer ends after the last valid
@@ -1546,50 +1548,80 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
         rmask + (int64_t)wd * a.N, (short)0, (int)(a.N * 4), 0x00020000);
     return rvalid ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(wrsrc, wvoff, 0, 0) : 0u;
   };
-  // The iterator runs one stage ahead of the copies: the stage after next is found after this
-  // stage's math, while its last matrix instructions drain.
-  int cur_j = -1, cur_s = 0;
-  uint32_t cur_act = 0u;
-  bool have = next_stage(cur_j, cur_s, cur_act);
+  // Only wave 0 walks the union; it publishes each stage as one word in a 4-slot LDS ring, three
+  // stages ahead of the stage being computed, and every wave reads the descriptor of the stage
+  // after next during this one.  The walk's scalar work then runs once per workgroup instead of
+  // in all eight waves, through the CU's one scalar unit, and no wave waits on the ring.
+  // Descriptor: bit 31 the stage exists, bits 23..30 its waves with math, bit 22 the stage within
+  // the block, bits 0..21 the block (M < 2^22).
+  uint32_t* ring = wmask + kWaves16 * W;
+  auto walk = [&]() -> uint32_t {
+    int j, s;
+    uint32_t act;
+    if (!next_stage(j, s, act)) return 0u;
+    return (1u << 31) | (act << 23) | ((uint32_t)s << 22) | (uint32_t)j;
+  };
+  auto d_j = [](uint32_t d) { return (int)(d & 0x3fffffu); };
+  auto d_s = [](uint32_t d) { return (int)((d >> 22) & 1u); };
+  auto d_act = [](uint32_t d) { return (d >> 23) & 0xffu; };
+  auto read_ring = [&](int slot) { return __builtin_amdgcn_readfirstlane(ring[slot]); };
+  if (wave == 0) {
+    const uint32_t w0d = walk();
+    const uint32_t w1d = w0d ? walk() : 0u;
+    const uint32_t w2d = w1d ? walk() : 0u;
+    if (lane == 0) {
+      ring[0] = w0d;
+      ring[1] = w1d;
+      ring[2] = w2d;
+    }
+  }
+  __syncthreads();
+  uint32_t dcur = read_ring(0), dnxt = read_ring(1);
   int mask_w = -1;
   uint32_t mask_word = 0u;
-  if (have) {
-    issue(cur_j, cur_s, 0, 0u);  // before the loop every wave takes its own share
-    mask_w = cur_j >> 5;
+  if (dcur) {
+    issue(d_j(dcur), d_s(dcur), 0, 0u);  // before the loop every wave takes its own share
+    mask_w = d_j(dcur) >> 5;
     mask_word = load_word(mask_w);
   }
-  int nj = -1, ns = 0;
-  uint32_t nact = 0u;
-  bool more = have && next_stage(nj, ns, nact);
   int buf = 0;
-  while (have) {
+  for (int i = 0; dcur; ++i) {
     wait_vmcnt<0>();
-    bar();  // publishes this stage's copy and retires the previous stage's buffer
+    bar();  // publishes this stage's copy and the ring word written during the previous stage
+    // the descriptor of the stage after next: loaded now, made scalar after the math, so that
+    // the LDS round trip overlaps the stage
+    const uint32_t dnn_v = dnxt ? ring[(i + 2) & 3] : 0u;
     int next_w = mask_w;
     uint32_t next_word = mask_word;
-    if (more) {
-      issue(nj, ns, buf ^ 1, cur_act);
-      if ((nj >> 5) != mask_w) {
-        next_w = nj >> 5;
+    if (dnxt) {
+      issue(d_j(dnxt), d_s(dnxt), buf ^ 1, d_act(dcur));
+      if ((d_j(dnxt) >> 5) != mask_w) {
+        next_w = d_j(dnxt) >> 5;
         next_word = load_word(next_w);
       }
     }
+    const int cur_j = d_j(dcur);
     const bool active = (mask_word >> (cur_j & 31)) & 1u;
-    const int r0 = cur_j * BLK + cur_s * kStage;
+    const int r0 = cur_j * BLK + d_s(dcur) * kStage;
     const int nvalid = (int)a.N - r0 < kStage ? (int)a.N - r0 : kStage;
     const lds_u8* base = smem + buf * kStageBytes;
     // a wave none of whose 16 rows keeps the block skips the stage's math
     if (__builtin_amdgcn_ballot_w64(active))
       exact_stage16<D>(base, base + kTileBytes, qf, active, nvalid, sl2, mrun, lsum, o,
                        fresh_lane());
+    const uint32_t dnn = __builtin_amdgcn_readfirstlane(dnn_v);
+    // three stages ahead, after the math; slot (i + 3) & 3 was last read three stages ago.  The
+    // write has completed before wave 0 reaches the next barrier (bar() has no fence).
+    if (wave == 0 && dnn) {
+      const uint32_t d3 = walk();
+      if (lane == 0) ring[(i + 3) & 3] = d3;
+      wait_lgkmcnt0();
+    }
     buf ^= 1;
-    cur_j = nj;
-    cur_s = ns;
-    cur_act = nact;
     mask_w = next_w;
     mask_word = next_word;
-    have = more;
-    if (have) more = next_stage(nj, ns, nact);
+    dcur = dnxt;
+    dnxt = dnn;
   }
   if (a.tile_kept && wave == 0) {  // blocks kept by some row of the tile
     int kept = 0;
@@ -1843,7 +1875,7 @@ static hipError_t launch_sparse_t(const SparseArgs& a, hipStream_t stream) {
 // workgroup's independent progress is worth more than the halved copy traffic.
 template <int D, int BLK>
 static hipError_t launch_sparse16_t(const SparseArgs& a, hipStream_t stream) {
-  const size_t smem = sparse_smem_bytes(D, a.Mp, 0) + (size_t)kWaves16 * (a.Mp / 32) * 4;
+  const size_t smem = sparse_smem_bytes(D, a.Mp, 0) + (size_t)kWaves16 * (a.Mp / 32) * 4 + 4 * 4;
   auto kern = sol_attn16_kernel<D, BLK>;
   hipError_t err = set_smem(kern, smem);
   if (err != hipSuccess) return err;
