@@ -1520,9 +1520,10 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
   // 64-bit product per stage (the head's end offset is fixed per tile).
   const int64_t end_bytes = (a.N - 1) * sn * 2 + D * 2;  // head start to the end of its last row
   const uint32_t sn2 = (uint32_t)(sn * 2);
-  auto issue = [&](int j, int s, int buf, uint32_t act) {
-    const uint32_t idle = ~act & ((1u << kWaves16) - 1u);
-    if (idle != 0u && wave != __builtin_ctz(idle)) return;
+  // imask: bit w set for the waves that issue; one bit (that wave issues the whole copy) or all
+  // eight (every wave issues its own share)
+  auto issue = [&](int j, int s, int buf, uint32_t imask) {
+    if (!((imask >> wave) & 1u)) return;
     const int64_t roff = ((int64_t)j * BLK + s * kStage) * sn;  // first row, in elements
     const int64_t rest = end_bytes - 2 * roff;
     const uint32_t bytes = (uint32_t)(rest < 0xffffffffll ? rest : 0xffffffffll);
@@ -1530,7 +1531,7 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     const i32x4_t vrs = make_rsrc(vb + roff, bytes);
     lds_u8* base = smem + buf * kStageBytes;
     const int lane_v = fresh_lane();
-    if (idle == 0u) {
+    if (imask == (1u << kWaves16) - 1u) {
       copy_share<D, kStage, NT>(krs, sn2, wave, lane_v, base);
       copy_share<D, kStage, NT>(vrs, sn2, wave, lane_v, base + kTileBytes);
       return;
@@ -1552,18 +1553,23 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
   // stages ahead of the stage being computed, and every wave reads the descriptor of the stage
   // after next during this one.  The walk's scalar work then runs once per workgroup instead of
   // in all eight waves, through the CU's one scalar unit, and no wave waits on the ring.
-  // Descriptor: bit 31 the stage exists, bits 23..30 its waves with math, bit 22 the stage within
-  // the block, bits 0..21 the block (M < 2^22).
+  // Descriptor: bit 31 the stage exists, bit 29 it runs past N, bits 17..24 the waves that issue
+  // the next stage's copy during it (the lowest wave without math alone, or all eight when every
+  // wave has math), bit 16 the stage within the block, bits 0..15 the block (M <= 2^16).
   uint32_t* ring = wmask + kWaves16 * W;
   auto walk = [&]() -> uint32_t {
     int j, s;
     uint32_t act;
     if (!next_stage(j, s, act)) return 0u;
-    return (1u << 31) | (act << 23) | ((uint32_t)s << 22) | (uint32_t)j;
+    const uint32_t idle = ~act & ((1u << kWaves16) - 1u);
+    const uint32_t imask = idle ? idle & (0u - idle) : (1u << kWaves16) - 1u;
+    const uint32_t partial = j * BLK + (s + 1) * kStage > (int)a.N ? 1u : 0u;
+    return (1u << 31) | (partial << 29) | (imask << 17) | ((uint32_t)s << 16) | (uint32_t)j;
   };
-  auto d_j = [](uint32_t d) { return (int)(d & 0x3fffffu); };
-  auto d_s = [](uint32_t d) { return (int)((d >> 22) & 1u); };
-  auto d_act = [](uint32_t d) { return (d >> 23) & 0xffu; };
+  auto d_j = [](uint32_t d) { return (int)(d & 0xffffu); };
+  auto d_s = [](uint32_t d) { return (int)((d >> 16) & 1u); };
+  auto d_imask = [](uint32_t d) { return (d >> 17) & 0xffu; };
+  auto d_partial = [](uint32_t d) { return ((d >> 29) & 1u) != 0u; };
   auto read_ring = [&](int slot) { return __builtin_amdgcn_readfirstlane(ring[slot]); };
   if (wave == 0) {
     const uint32_t w0d = walk();
@@ -1580,7 +1586,7 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
   int mask_w = -1;
   uint32_t mask_word = 0u;
   if (dcur) {
-    issue(d_j(dcur), d_s(dcur), 0, 0u);  // before the loop every wave takes its own share
+    issue(d_j(dcur), d_s(dcur), 0, (1u << kWaves16) - 1u);  // every wave takes its own share
     mask_w = d_j(dcur) >> 5;
     mask_word = load_word(mask_w);
   }
@@ -1588,13 +1594,14 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
   for (int i = 0; dcur; ++i) {
     wait_vmcnt<0>();
     bar();  // publishes this stage's copy and the ring word written during the previous stage
-    // the descriptor of the stage after next: loaded now, made scalar after the math, so that
-    // the LDS round trip overlaps the stage
-    const uint32_t dnn_v = dnxt ? ring[(i + 2) & 3] : 0u;
+    // the descriptor of the stage after next: loaded now (the slot is read even when there is no
+    // next stage; its word is then ignored), made scalar after the math, so that the LDS round
+    // trip overlaps the stage
+    const uint32_t dnn_v = ring[(i + 2) & 3];
     int next_w = mask_w;
     uint32_t next_word = mask_word;
     if (dnxt) {
-      issue(d_j(dnxt), d_s(dnxt), buf ^ 1, d_act(dcur));
+      issue(d_j(dnxt), d_s(dnxt), buf ^ 1, d_imask(dcur));
       if ((d_j(dnxt) >> 5) != mask_w) {
         next_w = d_j(dnxt) >> 5;
         next_word = load_word(next_w);
@@ -1602,14 +1609,13 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     }
     const int cur_j = d_j(dcur);
     const bool active = (mask_word >> (cur_j & 31)) & 1u;
-    const int r0 = cur_j * BLK + d_s(dcur) * kStage;
-    const int nvalid = (int)a.N - r0 < kStage ? (int)a.N - r0 : kStage;
+    const int nvalid = d_partial(dcur) ? (int)a.N - (cur_j * BLK + d_s(dcur) * kStage) : kStage;
     const lds_u8* base = smem + buf * kStageBytes;
     // a wave none of whose 16 rows keeps the block skips the stage's math
     if (__builtin_amdgcn_ballot_w64(active))
       exact_stage16<D>(base, base + kTileBytes, qf, active, nvalid, sl2, mrun, lsum, o,
                        fresh_lane());
-    const uint32_t dnn = __builtin_amdgcn_readfirstlane(dnn_v);
+    const uint32_t dnn = dnxt ? __builtin_amdgcn_readfirstlane(dnn_v) : 0u;
     // three stages ahead, after the math; slot (i + 3) & 3 was last read three stages ago.  The
     // write has completed before wave 0 reaches the next barrier (bar() has no fence).
     if (wave == 0 && dnn) {
