@@ -37,9 +37,11 @@
 //                    waves per SIMD.  In the pooled sweep each lane row's proxies are 8
 //                    consecutive blocks (selection bits by constant shifts, one 16-byte operand
 //                    read per pooled product) and a wave's union word is one DPP OR and store.
-//                    Stages are pipelined by hand, idle waves issue the next stage's copy, and
-//                    each tile's walk over its union starts at a point that lines up the tiles
-//                    running together on an XCD.
+//                    Stages are pipelined by hand.  Per-stage scalar work is kept to one wave
+//                    where it can be (the CU has one scalar unit): wave 0 alone walks the union
+//                    and publishes each stage as a word in an LDS ring, and the lowest wave
+//                    without math issues the whole next-stage copy.  Each tile's walk starts at
+//                    a point that lines up the tiles running together on an XCD.
 //   dense_attn_kernel the exact loop over every key: the reference the speedup is measured against.
 // The proxy map is never written to memory; only the optional debug outputs leave the kernel.
 #include <math.h>
@@ -1474,7 +1476,8 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
 
   // ---- exact attention over the kept blocks, double-buffered 64-key stages ----
   // Stage iterator over the union, with the set of waves that have math in each stage (bit w:
-  // some row of wave w keeps the block).  All values are wave-uniform.
+  // some row of wave w keeps the block).  All values are wave-uniform; only wave 0 runs it (see
+  // the descriptor ring below).
   // The walk over the union starts at block p0 and wraps around.  The i-th tile run on an XCD
   // starts at i * M / 64 (64 tiles run on an XCD at a time, started in turn): in the steady
   // state the tiles running together then sweep the same region of keys at the same time, so
