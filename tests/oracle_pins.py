@@ -258,6 +258,37 @@ def pin_select_matches_rows(lib):
     assert np.abs(oracle.dense_rows(q, k, v, rows=[3, 7], lib=lib)["out"] - ref[[3, 7]]).max() < 1e-12
 
 
+def pin_select_hand_examples(lib):
+    """The whole-head selection routine on the hand examples: every case's kept blocks, including
+    the exact ties (s = tau keeps the block), the population sigma and the hand-derived mu, sigma,
+    tau and smallest |s - tau|; and a q = 0 row (sigma = 0) keeps every block at finite beta."""
+    gd = json.load(open(GOLDEN))
+    for name, M in (("example1", 2), ("example2", 3)):
+        g = gd[name]
+        k = np.array(g["k"], np.float32)
+        q = (np.array(g["q"], np.float32) if "q" in g
+             else np.tile(np.array(g["q_row"], np.float32), (g["N"], 1)))
+        s = np.array(g["s"], np.float64)
+        for c in g["cases"]:
+            beta = _beta(c["beta"])
+            r = oracle.select(q, k, beta, g["block"], lib=lib)
+            keep = oracle.mask_bits(r["mask"], M).astype(int)
+            assert (keep == np.array(c["keep"])).all(), (name, c, keep)
+            tau = beta if math.isinf(beta) else g["mu"] + beta * g["sigma"]
+            assert np.abs(r["mu"] - g["mu"]).max() < 1e-15
+            assert np.abs(r["sigma"] - g["sigma"]).max() < 1e-14
+            if math.isinf(beta):
+                assert (r["tau"] == tau).all()
+            else:
+                assert np.abs(r["tau"] - tau).max() < 1e-14
+                assert np.abs(r["mindist"] - np.abs(s - tau).min()).max() < 1e-14
+    q, k, _ = _rand(1250, 40, 8)
+    q[3] = 0.0
+    for beta in (-1.0, 0.0, 2.5):
+        r = oracle.select(q, k, beta, 8, lib=lib)
+        assert oracle.mask_bits(r["mask"], 5)[3].all() and r["sigma"][3] == 0.0, beta
+
+
 def _route_brute(q, k, block, mode, param):
     """Top-k / top-p selection written from the definition with numpy: proxies from the exact
     logits (brute.proxy_scores), a stable sort, and a cumulative sum."""

@@ -19,6 +19,7 @@ MUTANTS = {
     "pooled_logit_uses_ln_block": ("s[j] + log((double)(hi - lo))", "s[j] + log((double)block)"),
     "sample_std": ("sqrt(m2 / (double)M);\n\n", "sqrt(m2 / (double)(M - 1));\n\n"),
     "strict_threshold": ("else sel[j] = s[j] >= t;", "else sel[j] = s[j] > t;"),
+    "select_strict_threshold": ("if (s[j] >= t) mask[i * W + j / 32]", "if (s[j] > t) mask[i * W + j / 32]"),
     "pool_divides_by_block": ("xbar[j * d + c] = sum / n;", "xbar[j * d + c] = sum / (double)block;"),
     "proxy_without_scale": ("s[j] = dot(qi, kbar + j * d, d) * inv_sqrt_d;\n\n        /* Step 2",
                             "s[j] = dot(qi, kbar + j * d, d);\n\n        /* Step 2"),
