@@ -88,6 +88,17 @@ def mfma_probe_tflops(sol, workgroups=2048, iters=1000, reps=3):
     return best
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, q, k, v, beta, F_tile, seconds=12.0):
     """The fp64 oracle on a bounded, seeded sample of query rows spread over every head, scaled to
     the same effective-TFLOP/s unit as the GPU value (F_tile x sampled fraction / oracle seconds).
@@ -130,6 +141,8 @@ def cpu_baseline(w, q, k, v, beta, F_tile, seconds=12.0):
         "value": F_tile * frac / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.threads(),
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": f"{n} of {total_rows} query rows ({per_head} seeded-uniform rows in each of the "
                   f"{H} heads of batch 0), full method per row incl. per-head K/V pooling, "
@@ -436,10 +449,22 @@ def main():
 
     dense_F = sol.dense_flops(B, H, N, d)
     pool_bytes = 2 * B * H * N * d * 2 + 2 * B * H * M * d * 4  # K,V read + Kbar,Vbar (fp32) written
-    # algorithmic work: 4*d FLOPs per (row, key) of every kept (128-row tile, block) pair; the
-    # matrix cores skip, per wave, blocks none of its rows keeps, so they execute F_exec
-    achieved = F_tile / (t_fused * 1e-3) / 1e12
+    # The fused kernel's matrix-core work as executed: the exact loop's 4*d FLOPs per (row, key) of
+    # each block some row of the row's wave keeps (a wave skips blocks none of its rows keeps:
+    # F_exec), plus the routing sweep's products over every padded block of every row -- the
+    # proxies from the three bf16 pieces of Kbar (3 x 2*d per row and block) and the pooled tokens'
+    # P Vbar (2*d per row and block; skipped in the drop ablation only).
+    Mp = (M + 31) // 32 * 32
+    F_route = 4 * 2.0 * B * H * N * Mp * d
+    F_mfma = F_exec + F_route
+    achieved = F_mfma / (t_fused * 1e-3) / 1e12
+    tile_rate = F_tile / (t_fused * 1e-3) / 1e12
     executed = F_exec / (t_fused * 1e-3) / 1e12
+    # minimum HBM bytes of the fused kernel: Q, K, V read once, O written once
+    min_bytes = 4.0 * B * H * N * d * 2
+    traffic = recorded_traffic(
+        [os.path.join(ROOT, "block_sparse_attention_sol_amd", "csrc", f)
+         for f in ("attn.hip", "common.hpp", "kernels.hpp")], w.name, beta)
     result = {
         "metric": METRIC,
         "value": F_tile / (t_sparse * 1e-3) / 1e12,
@@ -479,20 +504,35 @@ def main():
         "fused_executed_mfma_frac": executed / PEAK_BF16_TFLOPS,
         "pool_gbs": pool_bytes / (t_pool * 1e-3) / 1e9,
         "roofline": {
+            # algorithmically a dense contraction: F_mfma / min_bytes is thousands of FLOP per
+            # byte, far right of the ridge (2.5 PFLOP/s / 8 TB/s = 312 FLOP/B)
             "bound": "mfma",
             "achieved": achieved,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
             "measured_peak": probe,
             "frac_of_measured_peak": achieved / probe,
-            "traffic": recorded_traffic(
-                [os.path.join(ROOT, "block_sparse_attention_sol_amd", "csrc", f)
-                 for f in ("attn.hip", "common.hpp", "kernels.hpp")], w.name, beta),
+            "flops": "matrix-core FLOPs as executed per launch: exact loop at the kernel's wave "
+                     "granularity (F_exec) + routing sweep (three-piece proxies and pooled P Vbar "
+                     "over every padded block of every row)",
+            "executed_mfma_tflop": F_mfma / 1e12,
+            "routing_mfma_tflop": F_route / 1e12,
+            "tile_flops_rate": tile_rate,
+            "tile_flops_frac": tile_rate / PEAK_BF16_TFLOPS,
+            "min_hbm_bytes": min_bytes,
+            "traffic_gbs": None if traffic is None else traffic / (t_fused * 1e-3) / 1e9,
+            "traffic_frac_of_hbm_peak": None if traffic is None
+            else traffic / (t_fused * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            # what the measured bytes say: if moving them at the HBM peak takes longer than the
+            # executed FLOPs at the matrix peak, re-read traffic rather than the matrix cores
+            # limits the kernel
+            "measured_limiter": None if traffic is None else
+            ("hbm (re-read traffic)" if traffic / (PEAK_HBM_GBS * 1e9) > F_mfma / (PEAK_BF16_TFLOPS * 1e12)
+             else "mfma"),
             "kernel": ("sol_attn16_kernel<128,128>" if d == 128 else "sol_attn_kernel<64,64,4>")
                       + " (fused routing + pooled tokens + exact attention)",
-            "flops": "kept-block FLOPs F_tile: 4*d per (row, key) of each block some row of the "
-                     "row's 128-row query tile keeps",
         },
     }
     if not args.no_cpu_baseline:

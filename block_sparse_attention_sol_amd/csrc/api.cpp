@@ -39,7 +39,7 @@ int64_t padded_blocks(int64_t N, int block) { return (n_blocks(N, block) + 31) /
 
 // Offsets of the workspace regions (all 256-byte aligned).
 struct Workspace {
-  size_t kbar, kglob, kglob64, cp, kp, vbt, tau, rowmask, total;
+  size_t kbar, kglob, c64, f64top, ftop, cp, kp, vbt, tau, rowmask, total;
 };
 
 Workspace layout(const sol_shape& s, int block) {
@@ -49,8 +49,10 @@ Workspace layout(const sol_shape& s, int block) {
   Workspace w{};
   w.kbar = 0;
   w.kglob = w.kbar + align_up((size_t)(BH * M * s.d) * sizeof(float));
-  w.kglob64 = w.kglob + align_up((size_t)(BH * s.d) * sizeof(float));
-  w.cp = w.kglob64 + align_up((size_t)(BH * s.d) * sizeof(double));
+  w.c64 = w.kglob + align_up((size_t)(BH * s.d) * sizeof(double));
+  w.f64top = w.c64 + align_up((size_t)(BH * s.d * s.d) * sizeof(double));
+  w.ftop = w.f64top + align_up((size_t)(BH * solattn::kFactorTop * s.d) * sizeof(double));
+  w.cp = w.ftop + align_up((size_t)BH * sizeof(int32_t));
   w.kp = w.cp + align_up((size_t)(3 * BH * s.d * s.d) * sizeof(uint16_t));
   w.vbt = w.kp + align_up((size_t)(3 * BH * Mp * s.d) * sizeof(uint16_t));
   w.tau = w.vbt + align_up((size_t)(BH * s.d * Mp) * sizeof(uint16_t));
@@ -236,8 +238,10 @@ int attn_forward(const sol_shape* shape, const sol_strides* in_st, const sol_str
   const int64_t Mp = padded_blocks(shape->N, block);
   unsigned char* ws = (unsigned char*)workspace;
   float* kbar = (float*)(ws + w.kbar);
-  float* kglob = (float*)(ws + w.kglob);
-  double* kglob64 = (double*)(ws + w.kglob64);
+  double* kglob = (double*)(ws + w.kglob);
+  double* c64 = (double*)(ws + w.c64);
+  double* f64top = (double*)(ws + w.f64top);
+  int32_t* ftop = (int32_t*)(ws + w.ftop);
   uint16_t* cp = (uint16_t*)(ws + w.cp);
   uint16_t* kp = (uint16_t*)(ws + w.kp);
   uint16_t* vbt = (uint16_t*)(ws + w.vbt);
@@ -255,13 +259,15 @@ int attn_forward(const sol_shape* shape, const sol_strides* in_st, const sol_str
   if (e != hipSuccess) return hip_status(e, "pool kernel launch");
   if ((e = mark(1)) != hipSuccess) return hip_status(e, "event record");
   if (!mask_in) {
-    e = solattn::launch_kstats(d, BH, M, kbar, kglob, kglob64, cp, s);
+    e = solattn::launch_kstats(d, BH, M, kbar, kglob, c64, cp, f64top, ftop, s);
     if (e != hipSuccess) return hip_status(e, "pooled-key statistics launch");
     solattn::RowStatsArgs r{};
     r.q = (const uint16_t*)q;
     r.qs = ins;
     r.cp = cp;
     r.kglob = kglob;
+    r.f64top = f64top;
+    r.ftop = ftop;
     r.BH = BH;
     r.N = shape->N;
     r.beta = beta;

@@ -12,8 +12,10 @@
 // Kernels
 //   rowstats_kernel  mu_i = q_i . g / sqrt(d) and sigma_i^2 = q_i^T C q_i / d, where g and C are the
 //                    mean and covariance of the pooled keys: the mean and population variance of
-//                    the proxy row, exactly, without visiting its M entries.  C q is one bf16
-//                    matrix product per 32 rows over the hi + mid + lo pieces of C (fp32-accurate).
+//                    the proxy row, exactly, without visiting its M entries.  mu in fp64.  C q is
+//                    one bf16 matrix product per 32 rows over the hi + mid + lo pieces of C
+//                    (fp32-accurate), after C's dominant directions, if any, are split off and
+//                    taken in fp64 (see the pooled-key statistics).
 //                    Writes tau_i = mu_i + beta * sigma_i (-inf for the fused kernel where
 //                    sigma_i = 0: every proxy of such a row equals tau, so it keeps every block).
 //   sol_attn_kernel  (head dimension 64) one workgroup = 4 waves = 128 query rows of one
@@ -660,18 +662,22 @@ __global__ __launch_bounds__(kRowStatsThreads) void rowstats_kernel(RowStatsArgs
   const int lane = threadIdx.x & 63, c = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
 
-  // C pieces -> LDS, smallest first: tile p holds piece lo (p = 0), mid (1), hi (2); then kglob
+  // C pieces (dominant directions removed) -> LDS, smallest first: tile p holds piece lo (p = 0),
+  // mid (1), hi (2); then the mean pooled key and the dominant directions, both fp64
   const uint16_t* cbase = a.cp + bh * D * D;
   const int64_t piece = a.BH * D * D;
 #pragma unroll
   for (int p = 0; p < 3; ++p)
     load_tile<D, D, kRowStatsThreads>(cbase + (2 - p) * piece, 0, D, smem + p * D * D * 2);
-  float* kgl = (float*)(smem_raw + 3 * D * D * 2);
+  double* kgl = (double*)(smem_raw + 3 * D * D * 2);
+  double* ftl = kgl + D;  // [kFactorTop][D]
+  const int ntop = __builtin_amdgcn_readfirstlane(a.ftop[bh]);
   for (int i = threadIdx.x; i < D; i += kRowStatsThreads) kgl[i] = a.kglob[bh * D + i];
+  for (int i = threadIdx.x; i < kFactorTop * D; i += kRowStatsThreads)
+    ftl[i] = i < ntop * D ? a.f64top[bh * kFactorTop * D + i] : 0.0;
   wait_vmcnt<0>();
   __syncthreads();
 
-  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
   // C operand of (piece p, k step kk, row tile ab): row 32 ab + c, chunk 2 kk + h.  The row swizzle
   // reads row bits below 5 only, so ab and p add whole tiles and kk flips chunk bits:
   // offset = p D D 2 + ab 32 2D + (crel ^ (kk << 5)).
@@ -691,30 +697,21 @@ __global__ __launch_bounds__(kRowStatsThreads) void rowstats_kernel(RowStatsArgs
         __builtin_amdgcn_make_buffer_rsrc((void*)(qhead + row0w * a.qs.sn), (short)0, (int)bytes,
                                           0x00020000);
     const uint32_t qoff = (uint32_t)(c * a.qs.sn * 2);
+    // B operand of k step kk, lane half h: q at d = 16 kk + 4 h + 0..3 and 16 kk + 8 + 4 h + 0..3 (the
+    // pieces of C store their columns in the same order, see the pooled-key statistics).  These are
+    // exactly the rows of C q this lane half receives, so the same registers serve q^T (C q):
+    // element e of qf[kk] is q at d = 16 kk + 8 (e / 4) + 4 h + e % 4.
     bf16x8 qf[D / 16];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-      qf[kk] = __builtin_bit_cast(
-          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff + (16 * kk + 8 * h) * 2, 0, 0));
-    // query values in the layout of C q's rows (a = 32 ab + 8 g + 4 h + 0..3)
-    u32x2 qa[D / 32][4];
-#pragma unroll
-    for (int ab = 0; ab < D / 32; ++ab)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        qa[ab][g] = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_raw_buffer_load_b64(qrs, qoff + (32 * ab + 8 * g + 4 * h) * 2, 0, 0));
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const u32x2 lo = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_raw_buffer_load_b64(qrs, qoff + (16 * kk + 4 * h) * 2, 0, 0));
+      const u32x2 hi = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_raw_buffer_load_b64(qrs, qoff + (16 * kk + 8 + 4 * h) * 2, 0, 0));
+      qf[kk] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    }
     // all of the pass's loads are issued here, ahead of the matrix work that hides their latency
     __builtin_amdgcn_sched_barrier(0);
-    float mpart = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const float4 k0 = *reinterpret_cast<const float4*>(kgl + 16 * kk + 8 * h);
-      const float4 k1 = *reinterpret_cast<const float4*>(kgl + 16 * kk + 8 * h + 4);
-      const float kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mpart = fmaf((float)qf[kk][e], kv[e], mpart);
-    }
     // y[ab][v] = (C q)[32 ab + 8 (v/4) + 4 h + v%4]: D/32 independent accumulation chains,
     // pieces smallest first; the operand reads of step s + 1 are issued before step s's matrix
     // instructions
@@ -744,20 +741,51 @@ __global__ __launch_bounds__(kRowStatsThreads) void rowstats_kernel(RowStatsArgs
     }
     __builtin_amdgcn_sched_group_barrier(kSgMfma, D / 32, 0);
     __builtin_amdgcn_sched_barrier(0);
+    // q^T (C q) over this lane half's rows: y[ab][v] is row 32 ab + 8 g + 4 h + i (g = v / 4,
+    // i = v % 4), whose query element is element 4 (g % 2) + i of qf[2 ab + g / 2]
     float vpart = 0.f;
 #pragma unroll
     for (int ab = 0; ab < D / 32; ++ab)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        vpart = fmaf(y[ab][4 * g + 0], bf16_lo(qa[ab][g][0]), vpart);
-        vpart = fmaf(y[ab][4 * g + 1], bf16_hi(qa[ab][g][0]), vpart);
-        vpart = fmaf(y[ab][4 * g + 2], bf16_lo(qa[ab][g][1]), vpart);
-        vpart = fmaf(y[ab][4 * g + 3], bf16_hi(qa[ab][g][1]), vpart);
+      for (int v = 0; v < 16; ++v)
+        vpart = fmaf(y[ab][v], (float)qf[2 * ab + (v >> 3)][v & 7], vpart);
+    // q . g over this lane half's D/2 elements, in fp64 (products and sums of the bf16 query
+    // with the fp64 mean pooled key), and for heads with dominant directions (none for most) also
+    // w_k . q in fp64, their squares summed into vtop.  Each query element is
+    // converted where it is used, and the LDS offset is opaque to the optimiser, so that neither
+    // the converted query nor the fp64 operands are held in registers across the pass loop.
+    int hofs = 4 * h;
+    __asm__ __volatile__("" : "+v"(hofs));
+    double mpart = 0.0, vtop = 0.0;
+    if (ntop == 0) {
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          mpart = fma((double)(float)qf[kk][e], kgl[16 * kk + 8 * (e >> 2) + hofs + (e & 3)], mpart);
+    } else {
+      double z[kFactorTop] = {};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double qd = (double)(float)qf[kk][e];
+          const int idx = 16 * kk + 8 * (e >> 2) + hofs + (e & 3);
+          mpart = fma(qd, kgl[idx], mpart);
+#pragma unroll
+          for (int kt = 0; kt < kFactorTop; ++kt) z[kt] = fma(qd, ftl[kt * D + idx], z[kt]);
+        }
+#pragma unroll
+      for (int kt = 0; kt < kFactorTop; ++kt) {  // rows past ntop are zero in LDS
+        const double zz = z[kt] + __shfl_xor(z[kt], 32);
+        vtop = fma(zz, zz, vtop);
       }
-    const float mu = pair_sum(mpart) * inv_sqrt_d;
-    const float var = pair_sum(vpart) / (float)D;
+    }
+    const double mu64 = (mpart + __shfl_xor(mpart, 32)) / sqrt((double)D);
+    const float mu = (float)mu64;
+    const float var = (float)((vtop + (double)pair_sum(vpart)) / (double)D);
     const float sigma = sqrtf(fmaxf(var, 0.f));
-    const float tau = isinf(a.beta) ? a.beta : fmaf(a.beta, sigma, mu);
+    const float tau = isinf(a.beta) ? a.beta : (float)fma((double)a.beta, (double)sigma, mu64);
     // sigma = 0 (one key block, q = 0, or identical pooled keys): every proxy of the row equals
     // mu = tau, so s >= tau keeps every block and the row is dense.  The fused kernel's s and this
     // mu are rounded along different paths and need not compare equal, so the threshold it reads
@@ -1902,7 +1930,7 @@ hipError_t launch_sparse(int d, const SparseArgs& a, hipStream_t stream) {
 
 template <int D>
 static hipError_t launch_rowstats_t(const RowStatsArgs& a, hipStream_t stream) {
-  const size_t smem = (size_t)3 * D * D * 2 + D * sizeof(float);
+  const size_t smem = (size_t)3 * D * D * 2 + (size_t)(1 + kFactorTop) * D * sizeof(double);
   auto kern = rowstats_kernel<D>;
   hipError_t err = set_smem(kern, smem);
   if (err != hipSuccess) return err;

@@ -13,15 +13,24 @@ namespace solattn {
 hipError_t launch_pool(int d, int64_t BH, int64_t N, int block, const void* k, const void* v,
                        const Strides& kv, float* kbar, float* vbar, uint16_t* kp, uint16_t* vbt,
                        int64_t Mp, hipStream_t stream);
-// Mean (fp32 and fp64) and covariance (three bf16 pieces) of the pooled keys of every head.
-hipError_t launch_kstats(int d, int64_t BH, int64_t M, const float* kbar, float* kglob,
-                         double* kglob64, uint16_t* cp, hipStream_t stream);
+// Mean (fp64, kglob [BH][d]) and covariance (fp64, c64 [BH][d][d]) of the pooled keys of every
+// head, then the covariance's dominant directions w_k (k < ftop[bh], fp64, f64top
+// [BH][kFactorTop][d]) split off, C = sum_k w_k w_k^T + S, and the remainder S as three bf16 pieces
+// cp [3][BH][d][d].
+constexpr int kFactorTop = 4;          // at most this many factor rows in fp64
+constexpr double kDominant = 64.0;     // |w_k|^2 over the remaining mean diagonal: dominant
+hipError_t launch_kstats(int d, int64_t BH, int64_t M, const float* kbar, double* kglob,
+                         double* c64, uint16_t* cp, double* f64top, int32_t* ftop,
+                         hipStream_t stream);
 
 struct RowStatsArgs {
   const uint16_t* q;
   Strides qs;
-  const uint16_t* cp;     // [3][BH][d][d] covariance pieces (hi, mid, lo)
-  const float* kglob;     // [BH][d]
+  const uint16_t* cp;     // [3][BH][d][d] covariance with the dominant directions removed
+                          // (pieces hi, mid, lo)
+  const double* f64top;   // [BH][kFactorTop][d] the dominant directions w_k (fp64)
+  const int32_t* ftop;    // [BH] how many of them
+  const double* kglob;    // [BH][d] mean pooled key
   int64_t BH, N;
   float beta;
   float* tau;             // [BH][N] (workspace): selection threshold, -inf where sigma = 0

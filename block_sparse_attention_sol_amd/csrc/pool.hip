@@ -14,9 +14,9 @@
 //   vbt  [BH][d][Mp] bf16: Vbar transposed (block index contiguous), the A operand of the
 //        pooled tokens' P Vbar product;
 // where Mp = M rounded up to a multiple of 32; padding blocks are written as zeros.
-// A small per-head kernel follows: the mean pooled key (fp32 and fp64) and the covariance matrix
-// of the pooled keys as three bf16 pieces, from which every query's proxy standard deviation is a
-// quadratic form.
+// Two small per-head kernels follow: the mean pooled key and the covariance matrix C of the pooled
+// keys (fp64), from which every query's proxy variance is the quadratic form q^T C q / d; then the
+// removal of C's dominant directions, if any, so that the form stays well conditioned.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -102,17 +102,15 @@ __global__ __launch_bounds__(kThreads) void pool_kv_kernel(
 // Mean and covariance of the pooled keys of each head, in fp64:
 //   g[a] = (1/M) sum_j Kbar_j[a],   C[a][b] = (1/M) sum_j Kbar_j[a] Kbar_j[b] - g[a] g[b].
 // The mean proxy score of a query is q . g / sqrt(d) (the mean is linear), and for the proxy row
-// s_ij = q_i . Kbar_j / sqrt(d) the population variance over j is exactly q_i^T C q_i / d.  C is
-// rounded to fp32 and written as hi + mid + lo bf16 pieces cp [3][BH][D][D] (their sum is the fp32
-// value), so a bf16 matrix product with fp32 accumulation evaluates C q to fp32 accuracy.
+// s_ij = q_i . Kbar_j / sqrt(d) the population variance over j is exactly q_i^T C q_i / d.
+// Writes g and C (fp64; C as [BH][D][D]) for the factorisation below.
 // One workgroup computes a 32 x 32 tile of C: pooled keys are staged through LDS in chunks of 64
 // blocks, each thread accumulates a 2 x 2 block of products and the two column sums.  The diagonal
-// tiles (ai == bi) also write g (fp32 and fp64).
+// tiles (ai == bi) also write g.
 template <int D>
 __global__ __launch_bounds__(kThreads) void kstats_kernel(const float* __restrict__ kbar, int64_t M,
-                                                          float* __restrict__ kglob,
-                                                          double* __restrict__ kglob64,
-                                                          uint16_t* __restrict__ cp) {
+                                                          double* __restrict__ kglob,
+                                                          double* __restrict__ c64) {
   constexpr int kT = D / 32;  // tiles per dimension
   constexpr int kChunk = 64;
   __shared__ double sa[kChunk][32];
@@ -153,13 +151,9 @@ __global__ __launch_bounds__(kThreads) void kstats_kernel(const float* __restric
   if (t < 32) {
     ga[t] = s1a / (double)M;
     gb[t] = s1b / (double)M;
-    if (ai == bi) {
-      kglob[bh * D + 32 * ai + t] = (float)(s1a / (double)M);
-      kglob64[bh * D + 32 * ai + t] = s1a / (double)M;
-    }
+    if (ai == bi) kglob[bh * D + 32 * ai + t] = s1a / (double)M;
   }
   __syncthreads();
-  const int64_t BH = gridDim.x / (kT * kT);
   const double inv_m = 1.0 / (double)M;
   const double cv[2][2] = {{c00, c01}, {c10, c11}};
 #pragma unroll
@@ -167,15 +161,131 @@ __global__ __launch_bounds__(kThreads) void kstats_kernel(const float* __restric
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
       const int ra = 2 * ta + x, rb = 2 * tb + y;
-      const float c = (float)(cv[x][y] * inv_m - ga[ra] * gb[rb]);
-      const uint16_t h16 = f32_to_bf16_rne(c);
-      const float r1 = c - bits_f32((uint32_t)h16 << 16);
+      c64[(bh * D + 32 * ai + ra) * D + 32 * bi + rb] = cv[x][y] * inv_m - ga[ra] * gb[rb];
+    }
+}
+
+// Dominant directions of each head's pooled-key covariance, removed before the quadratic form.
+// The row statistics evaluate sigma_i^2 d = q^T C q on the matrix cores (fp32-accurate), whose
+// rounding error scales with |q|^T |C| |q| rather than with q^T C q: when C has a direction far
+// stronger than the others and q is nearly orthogonal to it, the relative error grows by the ratio
+// of the two.  Such directions are split off by steps of Cholesky with diagonal pivoting in fp64,
+//   C = sum_{k<T} w_k w_k^T + S_T,
+// and q^T C q = sum_k (w_k . q)^2 + q^T S_T q, the w_k . q taken in fp64 by the row statistics and
+// the well-conditioned remainder S_T on the matrix cores.  Step k (pivot: the largest remaining
+// diagonal entry, lowest index on ties) is taken only while its row is dominant, |w_k|^2 >
+// kDominant * trace(S_{k+1}) / D, and at most kFactorTop times.  On the synthetic video-token
+// workloads this ratio is 4-11 (no step taken); one strong key direction gives ~10^5.
+// Writes w_k (fp64) to f64top [BH][kFactorTop][D], T to ftop [BH], and S_T as three bf16 pieces
+// (hi, mid, lo; their sum is the fp32 value) to cp [3][BH][D][D], each row's columns in the order
+// the row statistics take the query in: column b at position b with bits 2 and 3 swapped (so the
+// 16-byte chunk 2 kk + h of a row holds columns 16 kk + 4 h + 0..3 and 16 kk + 8 + 4 h + 0..3).
+// One workgroup per head: thread t owns the TB x TB block (t / 16, t % 16) of S in registers.
+template <int D>
+__global__ __launch_bounds__(kThreads) void kdeflate_kernel(const double* __restrict__ c64,
+                                                            uint16_t* __restrict__ cp,
+                                                            double* __restrict__ f64top,
+                                                            int32_t* __restrict__ ftop, int64_t BH) {
+  constexpr int TB = D / 16;  // block edge
+  static_assert(kThreads == 256, "a 16 x 16 grid of blocks");
+  __shared__ double dg[D];    // remaining diagonal (-inf once pivoted)
+  __shared__ double col[D];   // pivot column
+  const int64_t bh = blockIdx.x;
+  const int t = threadIdx.x;
+  const int br = t / 16, bc = t % 16;
+  const int lane = t & 63;
+  const double* C = c64 + bh * D * D;
+  double S[TB][TB];
+#pragma unroll
+  for (int i = 0; i < TB; ++i)
+#pragma unroll
+    for (int j = 0; j < TB; ++j) S[i][j] = C[(br * TB + i) * D + bc * TB + j];
+  uint32_t piv_r = 0u, piv_c = 0u;  // pivoted rows / columns among this thread's TB
+  if (br == bc) {
+#pragma unroll
+    for (int i = 0; i < TB; ++i) dg[br * TB + i] = S[i][i];
+  }
+  __syncthreads();
+  double* F64 = f64top + bh * kFactorTop * D;
+  int k = 0;
+  for (; k < kFactorTop; ++k) {
+    // pivot: argmax of the remaining diagonal, lowest index on ties (each wave reduces all D)
+    double bv = -INFINITY;
+    int bi = D;
+    for (int i = lane; i < D; i += 64) {
+      const double x = dg[i];
+      if (x > bv) { bv = x; bi = i; }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    const int p = __builtin_amdgcn_readfirstlane(bi);
+    const double dmax = bv;
+    if (!(dmax > 0.0)) break;  // uniform: every wave reduced the same values
+    if (bc == p / TB) {
+#pragma unroll
+      for (int i = 0; i < TB; ++i) col[br * TB + i] = S[i][p % TB];
+    }
+    __syncthreads();
+    // |w|^2 and the remaining trace, summed by every thread in the same order (same decision)
+    const double rs = 1.0 / sqrt(dmax);
+    double nw = 0.0, tr = 0.0;
+    for (int i = 0; i < D; ++i) {
+      const double di = dg[i];
+      if (di != -INFINITY) {
+        const double wi = i == p ? sqrt(dmax) : col[i] * rs;
+        nw = fma(wi, wi, nw);
+        tr += di;
+      }
+    }
+    if (!(nw > kDominant * (tr - nw) / (double)D)) break;  // uniform
+    double wr[TB], wc[TB];
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      const int r = br * TB + i, c = bc * TB + i;
+      wr[i] = ((piv_r >> i) & 1u) ? 0.0 : (r == p ? sqrt(dmax) : col[r] * rs);
+      wc[i] = ((piv_c >> i) & 1u) ? 0.0 : (c == p ? sqrt(dmax) : col[c] * rs);
+    }
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+#pragma unroll
+      for (int j = 0; j < TB; ++j) S[i][j] = fma(-wr[i], wc[j], S[i][j]);
+    if (br == p / TB) piv_r |= 1u << (p % TB);
+    if (bc == p / TB) piv_c |= 1u << (p % TB);
+    __syncthreads();  // every thread has read dg and col of this step
+    if (br == bc) {
+#pragma unroll
+      for (int i = 0; i < TB; ++i) dg[br * TB + i] = ((piv_r >> i) & 1u) ? -INFINITY : S[i][i];
+    }
+    if (bc == 0) {
+#pragma unroll
+      for (int i = 0; i < TB; ++i) F64[k * D + br * TB + i] = wr[i];
+    }
+    __syncthreads();
+  }
+  if (t == 0) ftop[bh] = k;
+  // S_T in three bf16 pieces; pivoted rows and columns are exactly zero in exact arithmetic and
+  // are written as zero
+  const int64_t piece = BH * D * D;
+  uint16_t* P = cp + bh * D * D;
+#pragma unroll
+  for (int i = 0; i < TB; ++i)
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      const bool zero = ((piv_r >> i) & 1u) || ((piv_c >> j) & 1u);
+      const float x = zero ? 0.f : (float)S[i][j];
+      const uint16_t h16 = f32_to_bf16_rne(x);
+      const float r1 = x - bits_f32((uint32_t)h16 << 16);
       const uint16_t m16 = f32_to_bf16_rne(r1);
       const uint16_t l16 = f32_to_bf16_rne(r1 - bits_f32((uint32_t)m16 << 16));
-      const int64_t off = (bh * D + 32 * ai + ra) * D + 32 * bi + rb;
-      cp[0 * BH * D * D + off] = h16;
-      cp[1 * BH * D * D + off] = m16;
-      cp[2 * BH * D * D + off] = l16;
+      const int b = bc * TB + j;
+      const int64_t off = (int64_t)(br * TB + i) * D + ((b & ~12) | ((b & 4) << 1) | ((b & 8) >> 1));
+      P[off] = h16;
+      P[piece + off] = m16;
+      P[2 * piece + off] = l16;
     }
 }
 
@@ -197,14 +307,20 @@ hipError_t launch_pool(int d, int64_t BH, int64_t N, int block, const void* k, c
   return hipGetLastError();
 }
 
-hipError_t launch_kstats(int d, int64_t BH, int64_t M, const float* kbar, float* kglob,
-                         double* kglob64, uint16_t* cp, hipStream_t stream) {
-  if (d == 64)
+hipError_t launch_kstats(int d, int64_t BH, int64_t M, const float* kbar, double* kglob,
+                         double* c64, uint16_t* cp, double* f64top, int32_t* ftop,
+                         hipStream_t stream) {
+  if (d == 64) {
     hipLaunchKernelGGL(kstats_kernel<64>, dim3((unsigned)(BH * 4)), dim3(kThreads), 0, stream,
-                       kbar, M, kglob, kglob64, cp);
-  else
+                       kbar, M, kglob, c64);
+    hipLaunchKernelGGL(kdeflate_kernel<64>, dim3((unsigned)BH), dim3(kThreads), 0, stream, c64, cp,
+                       f64top, ftop, BH);
+  } else {
     hipLaunchKernelGGL(kstats_kernel<128>, dim3((unsigned)(BH * 16)), dim3(kThreads), 0, stream,
-                       kbar, M, kglob, kglob64, cp);
+                       kbar, M, kglob, c64);
+    hipLaunchKernelGGL(kdeflate_kernel<128>, dim3((unsigned)BH), dim3(kThreads), 0, stream, c64, cp,
+                       f64top, ftop, BH);
+  }
   return hipGetLastError();
 }
 

@@ -140,3 +140,34 @@ def random_qkv(B: int, H: int, N: int, d: int, seed: int = 0, scale: float = 1.0
     t = [torch.from_numpy((scale * rng.standard_normal((B, H, N, d))).astype(np.float32))
          .to(torch.bfloat16) for _ in range(3)]
     return t[0], t[1], t[2]
+
+
+def anisotropic_qkv(B: int, H: int, N: int, d: int, seed: int = 0, strength: float = 24.0,
+                    noise: float = 0.5, leak: float = 0.02):
+    """Keys with one strong shared direction, queries nearly orthogonal to it (bf16 tensors
+    [B, H, N, d]): a hard case for the proxy-row statistics.
+
+    Per head: a random unit direction u (not aligned with any axis); K = noise * N(0, 1)
+    + c_n u with c_n = strength * sin(2 pi * 3 n / N + phase), so block means of K vary strongly
+    along u from block to block; Q = N(0, 1) with its component along u replaced by
+    leak * N(0, 1); V = N(0, 1).  The proxy rows then have a small spread set by the noise,
+    beside a pooled-key covariance whose largest eigenvalue is strength^2 / 2."""
+    import torch
+
+    rng = np.random.default_rng(seed)
+    q = np.empty((B, H, N, d), np.float32)
+    k = np.empty_like(q)
+    v = np.empty_like(q)
+    n = np.arange(N, dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            u = rng.standard_normal(d)
+            u /= np.linalg.norm(u)
+            c = strength * np.sin(2.0 * math.pi * 3.0 * n / N + rng.uniform(0.0, 2.0 * math.pi))
+            k[b, h] = noise * rng.standard_normal((N, d)) + c[:, None] * u[None, :]
+            qq = rng.standard_normal((N, d))
+            qq -= (qq @ u)[:, None] * u[None, :]
+            qq += leak * rng.standard_normal(N)[:, None] * u[None, :]
+            q[b, h] = qq
+            v[b, h] = rng.standard_normal((N, d))
+    return tuple(torch.from_numpy(x).to(torch.bfloat16) for x in (q, k, v))

@@ -69,7 +69,7 @@ def test_workspace_bytes(lib):
     n = lib.sol_attn_workspace_bytes(ctypes.byref(s), 128)
     M = math.ceil(75600 / 128)
     Mp = math.ceil(M / 32) * 32
-    lower = (40 * M * 128 * 4 + 40 * 128 * 4 + 40 * 128 * 8 + 3 * 40 * 128 * 128 * 2
+    lower = (40 * M * 128 * 4 + 40 * 128 * 8 + 40 * 128 * 128 * 8 + 40 * 4 * 128 * 8 + 40 * 4 + 3 * 40 * 128 * 128 * 2
              + 3 * 40 * Mp * 128 * 2 + 40 * Mp * 128 * 2 + 40 * 75600 * 4 + 40 * 75600 * (Mp // 32) * 4)
     assert lower <= n <= lower + 8 * 256
     assert lib.sol_attn_workspace_bytes(ctypes.byref(_shape(d=96)), 128) == 0

@@ -92,6 +92,7 @@ def _sparse_vs_oracle(sol, q, k, v, beta, block, rows_per_head=None, heads=None,
     B, H, N, d = q.shape
     heads = range(H) if heads is None else heads
     worst = (0.0, 0.0)
+    stats_worst = 0.0
     for h in full_mask_heads:
         # the whole selection mask of the head (every row, every block)
         qh, kh, vh = _np(q[0, h]), _np(k[0, h]), _np(v[0, h])
@@ -115,19 +116,50 @@ def _sparse_vs_oracle(sol, q, k, v, beta, block, rows_per_head=None, heads=None,
             assert_close(got, ref["out"], f"{what} b{b} h{h} (oracle mask)")
             assert_close_bf16_output(_np(out[b, h])[rows], ref["out"], f"{what} b{b} h{h} (bf16)")
             worst = (max(worst[0], ma), max(worst[1], mr))
-            # row statistics
-            for key in ("mu", "sigma"):
-                g = dbg[key][b, h].cpu().numpy()[rows].astype(np.float64)
-                assert np.all(np.abs(g - ref[key]) <= 2e-5 * np.maximum(1.0, np.abs(ref[key]))), key
-            if math.isfinite(beta):
-                g = dbg["tau"][b, h].cpu().numpy()[rows].astype(np.float64)
-                assert np.all(np.abs(g - ref["tau"]) <= 2e-5 * np.maximum(1.0, np.abs(ref["tau"])))
+            kabs = np.abs(oracle.pool(kh, block)).max(axis=0)
+            stats_worst = max(stats_worst, check_row_stats(dbg, b, h, rows, ref, beta, what,
+                                                           kbar_absmax=kabs, q=qh))
             lse_g = dbg["lse"][b, h].cpu().numpy()[rows]
             lse_err = float(np.abs(lse_g - ref_g["lse"]).max())
             _log(f"{what} b{b} h{h}: max-abs {ma:.3e} mean-rel {mr:.3e} lse {lse_err:.2e}")
             assert lse_err < LSE_TOL
-    _log(f"{what}: worst max-abs {worst[0]:.3e} mean-rel {worst[1]:.3e}")
+    _log(f"{what}: worst max-abs {worst[0]:.3e} mean-rel {worst[1]:.3e}, "
+         f"row statistics within {stats_worst:.2e} of the row RMS")
     return out, dbg
+
+
+# Row statistics bar.  mu, sigma and tau are statistics of the row's proxy scores, so their errors
+# are measured against the row's scale, the RMS of its proxies sqrt(mu^2 + sigma^2) (for tau, times
+# 1 + |beta|): relative error <= 1e-6 of that scale, plus the first-order effect of the pooled keys
+# being fp32 (the precision of the pooled tensors; the mean over a block whose token count is not
+# a power of two rounds): with Kbar_j carrying relative rounding u = 2^-24 per element, mu and sigma
+# move by at most u * E_i, and with twice that allowed,
+#   |err| <= 1e-6 * rms_i + 2 u E_i,   E_i = sum_l |q_il| max_j |Kbar_jl| / sqrt(d).
+# The second term matters only for rows whose proxies nearly cancel (rms_i far below E_i, e.g. a
+# single key block with q almost orthogonal to its mean); a bar relative to sigma alone would be
+# ill-posed for rows whose proxies share a large common offset, and one relative to tau for rows
+# where mu and beta sigma cancel.  The log reports the error against 1e-6 * rms_i alone.
+STATS_REL = 1e-6
+U32 = 2.0 ** -24
+
+
+def check_row_stats(dbg, b, h, rows, ref, beta, what="", kbar_absmax=None, q=None):
+    rms = np.sqrt(ref["mu"] ** 2 + ref["sigma"] ** 2)
+    d = q.shape[1]
+    E = (np.abs(q[rows].astype(np.float64)) @ kbar_absmax) / math.sqrt(d)
+    worst = 0.0
+    for key in ("mu", "sigma", "tau"):
+        if key == "tau" and not math.isfinite(beta):
+            continue
+        g = dbg[key][b, h].cpu().numpy()[rows].astype(np.float64)
+        f = (1.0 + abs(beta)) if key == "tau" else 1.0
+        e = np.abs(g - ref[key])
+        bar = f * (STATS_REL * rms + 2.0 * U32 * E)
+        ok = e <= bar
+        assert ok.all(), (f"{what} b{b} h{h}: {key} error {float(e[~ok].max()):.3e} above its bar "
+                          f"{float(bar[~ok][np.argmax(e[~ok])]):.3e} (row scale {float(rms[~ok][np.argmax(e[~ok])]):.3e})")
+        worst = max(worst, float((e / np.maximum(f * STATS_REL * rms, 1e-300)).max()) * STATS_REL)
+    return worst
 
 
 @pytest.mark.parametrize("beta", [0.5, -INF, INF, 0.0, 1.5, -0.7])
@@ -269,15 +301,53 @@ def test_wan_dense_full_shape(sol, wan_inputs):
         _log(f"wan dense h{h}: max-abs {ma:.3e} mean-rel {mr:.3e}")
 
 
-@pytest.mark.parametrize("name,heads,beta", [("hunyuan", 3, 2.2), ("long", 3, 2.7)])
-def test_long_workloads_subset_of_heads(sol, name, heads, beta):
-    """HunyuanVideo shape (N=118800, last block 16 tokens) and the long-video shape (N=219600,
-    per-head amplitude U(1,3)): the first heads of the full seeded draw, full per-head size."""
+@pytest.fixture(scope="module")
+def hunyuan_inputs():
     from block_sparse_attention_sol_amd import synth
-    _log(f"{name}: generating {heads} heads")
-    q, k, v = (t.cuda() for t in synth.generate(name, heads=heads))
-    _sparse_vs_oracle(sol, q, k, v, beta, 128, rows_per_head=300, heads=list(range(heads)),
-                      what=f"{name} beta={beta}", full_mask_heads=[0])
+    _log("generating the HunyuanVideo-shape workload (33x45x80 grid, 24 heads, d=128)")
+    return tuple(t.cuda() for t in synth.generate("hunyuan"))
+
+
+# The betas the benchmark calibrates for the HunyuanVideo shape (kept-block densities 10%, 15% and
+# 25% at 128-row query tiles) and for the long-video shape (8%).
+@pytest.mark.parametrize("beta", [2.539, 2.232, 1.927])
+def test_hunyuan_operating_points(sol, hunyuan_inputs, beta):
+    """HunyuanVideo shape (N=118800, last block 16 tokens), all 24 heads launched: sampled rows of
+    6 heads and the full mask of one, at each benchmarked density."""
+    q, k, v = hunyuan_inputs
+    _log(f"hunyuan beta={beta}")
+    _sparse_vs_oracle(sol, q, k, v, beta, 128, rows_per_head=300, heads=[0, 5, 9, 13, 18, 23],
+                      what=f"hunyuan beta={beta}", full_mask_heads=[0])
+
+
+def test_long_operating_point(sol):
+    """Long-video shape (N=219600, per-head amplitude U(1,3)) at its benchmarked beta: the first 27
+    heads of the seeded draw (which hold the smallest and the largest amplitude, heads 11 and 26),
+    sampled rows of 6 heads including those two, and the full mask of the largest-amplitude head."""
+    from block_sparse_attention_sol_amd import synth
+    beta = 2.781
+    w = synth.WORKLOADS["long"]
+    A = synth.amplitudes(w, np.random.default_rng(0))
+    lo, hi = int(np.argmin(A)), int(np.argmax(A))
+    heads = sorted({0, 4, 13, 20, lo, hi})
+    _log(f"long: generating {hi + 1} heads (amplitude min at head {lo}, max at head {hi})")
+    q, k, v = (t.cuda() for t in synth.generate("long", heads=hi + 1))
+    _sparse_vs_oracle(sol, q, k, v, beta, 128, rows_per_head=250, heads=heads,
+                      what=f"long beta={beta}", full_mask_heads=[hi])
+
+
+@pytest.mark.parametrize("N,d,block,beta", [(4096, 128, 128, 1.0), (4096, 128, 128, -0.5),
+                                            (3000, 64, 64, 1.5), (5000, 128, 64, 0.3)])
+def test_anisotropic_keys(sol, N, d, block, beta):
+    """Keys with one strong direction that varies from block to block, queries nearly orthogonal to
+    it: the pooled-key covariance has one eigenvalue ~10^4-10^5 times the rest, and each row's
+    proxy spread comes from the small directions.  Full masks against the oracle, row statistics
+    at the 1e-6 bar, outputs on every row."""
+    from block_sparse_attention_sol_amd import synth
+    _log(f"anisotropic keys N={N} d={d} block={block} beta={beta}")
+    q, k, v = (t.cuda() for t in synth.anisotropic_qkv(1, 2, N, d, seed=N + d, strength=48.0))
+    _sparse_vs_oracle(sol, q, k, v, beta, block, what=f"anisotropic N={N} d={d}",
+                      full_mask_heads=[0, 1])
 
 
 def test_determinism(sol):
@@ -295,17 +365,20 @@ def test_determinism(sol):
     assert torch.equal(c, e)
 
 
-def test_drop_ablation(sol):
-    """Dropping unselected blocks (ablation flag) matches the oracle's drop mode."""
-    _log("drop ablation")
-    q, k, v = _qkv(1, 2, 900, 64, seed=21, scale=1.3)
-    out, _ = sol.attn_fwd(q, k, v, 0.2, 64, drop_unselected=True)
-    out2, dbg = sol.attn_fwd(q, k, v, 0.2, 64, debug=True)
+@pytest.mark.parametrize("N,d,block,beta", [(900, 64, 64, 0.2), (1000, 128, 128, 0.6),
+                                            (2100, 128, 128, 2.2), (777, 128, 64, 1.0)])
+def test_drop_ablation(sol, N, d, block, beta):
+    """Dropping unselected blocks (ablation flag) matches the oracle's drop mode, through the
+    threshold path of both fused kernels (d = 64 and the 16-row kernel at d = 128)."""
+    _log(f"drop ablation N={N} d={d} block={block} beta={beta}")
+    q, k, v = _qkv(1, 2, N, d, seed=21 + N, scale=1.3)
+    out, _ = sol.attn_fwd(q, k, v, beta, block, drop_unselected=True)
+    out2, dbg = sol.attn_fwd(q, k, v, beta, block, debug=True)
     torch.cuda.synchronize()
     for h in range(2):
         gmask = dbg["mask"][0, h].cpu().numpy().view(np.uint32)
-        r = oracle.attn_rows(_np(q[0, h]), _np(k[0, h]), _np(v[0, h]), 0.2, 64, mask_override=gmask,
-                             drop=True)
+        r = oracle.attn_rows(_np(q[0, h]), _np(k[0, h]), _np(v[0, h]), beta, block,
+                             mask_override=gmask, drop=True)
         ok = ~np.isnan(r["out"][:, 0])
         assert_close_bf16_output(_np(out[0, h])[ok], r["out"][ok], f"drop h{h}")
         assert (_np(out[0, h])[~ok] == 0).all()
