@@ -402,6 +402,46 @@ int sol_select_topp(const sol_shape* shape, int block, const float* s_map, float
   return route_select(shape, block, s_map, 1, 0, p, mask, stream);
 }
 
+int sol_attn_fwd_noalloc(const sol_shape* shape, const void* q, const void* k, const void* v,
+                         float beta, int block, void* out, void* stream) {
+  static_assert(SOL_NOALLOC_SCRATCH_BYTES == solattn::kNoAllocScratchBytes,
+                "the header states the scratch size");
+  int st;
+  if ((st = check_shape(shape)) || (st = check_block(block))) return st;
+  if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
+      (st = check_tensor(out, "out")))
+    return st;
+  if (std::isnan(beta)) return fail(SOL_EINVAL, "beta is NaN");
+  const size_t ext = extent_bytes(*shape, contiguous(*shape));
+  if (overlaps(out, ext, q, ext) || overlaps(out, ext, k, ext) || overlaps(out, ext, v, ext))
+    return fail(SOL_EINVAL, "out overlaps an input");
+  // Heads are independent: run them in the largest groups whose workspace fits the scratch.
+  const int64_t BH = shape->B * shape->H;
+  const size_t cap = solattn::kNoAllocScratchBytes;
+  auto need = [&](int64_t g) { return layout(sol_shape{1, g, shape->N, shape->d}, block).total; };
+  if (need(1) > cap)
+    return fail(SOL_EWORKSPACE,
+                "one head needs %zu bytes of workspace; the allocation-free call holds %zu "
+                "(use sol_attn_fwd with a caller workspace)", need(1), cap);
+  int64_t G = (int64_t)(cap / need(1));
+  if (G > BH) G = BH;
+  while (G > 1 && need(G) > cap) --G;
+  void* scratch = nullptr;
+  hipError_t e = solattn::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, "scratch address lookup");
+  const int64_t head_elems = shape->N * shape->d;
+  for (int64_t h0 = 0; h0 < BH; h0 += G) {
+    const int64_t g = BH - h0 < G ? BH - h0 : G;
+    const sol_shape sub{1, g, shape->N, shape->d};
+    const int64_t off = h0 * head_elems;
+    st = attn_forward(&sub, nullptr, nullptr, (const uint16_t*)q + off, (const uint16_t*)k + off,
+                      (const uint16_t*)v + off, beta, block, (uint16_t*)out + off, scratch, cap,
+                      nullptr, nullptr, 0, stream);
+    if (st != SOL_OK) return st;
+  }
+  return ok();
+}
+
 int sol_attn_fwd(const sol_shape* shape, const void* q, const void* k, const void* v, float beta,
                  int block, void* out, void* workspace, size_t workspace_bytes, void* stream) {
   return sol_attn_fwd_ex(shape, q, k, v, beta, block, out, workspace, workspace_bytes, nullptr,

@@ -79,6 +79,11 @@ hipError_t launch_route_select(int mode, const float* s_map, int64_t BH, int64_t
                                int block, int64_t k, float p, uint32_t* mask, hipStream_t stream);
 int64_t route_max_blocks();  // largest M the selection kernel holds in registers
 
+// The allocation-free call's workspace: a file-scope device array of kNoAllocScratchBytes per GPU
+// (SOL_NOALLOC_SCRATCH_BYTES in the public header); *ptr receives the current device's copy.
+constexpr size_t kNoAllocScratchBytes = size_t(256) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Matrix-core rate probe: `workgroups` x 4 waves, each issuing iters x mfma_probe_chains()
 // independent bf16 32x32x16 MFMAs.
 hipError_t launch_mfma_probe(int workgroups, int iters, float* sink, hipStream_t stream);

@@ -26,6 +26,7 @@ EXPORTS = (
     "sol_pool_kv",
     "sol_attn_fwd",
     "sol_attn_fwd_ex",
+    "sol_attn_fwd_noalloc",
     "sol_attn_fwd_masked",
     "sol_proxy_map",
     "sol_select_topk",
@@ -84,6 +85,7 @@ def load_library(path: str = LIB_PATH):
     lib.sol_attn_fwd.argtypes = [shp, vp, vp, vp, cf, ci, vp, vp, sz, vp]
     lib.sol_attn_fwd_ex.argtypes = [shp, vp, vp, vp, cf, ci, vp, vp, sz,
                                     ctypes.POINTER(SolAttnDebug), vp]
+    lib.sol_attn_fwd_noalloc.argtypes = [shp, vp, vp, vp, cf, ci, vp, vp]
     lib.sol_dense_fwd.argtypes = [shp, vp, vp, vp, vp, vp, vp]
     lib.sol_mfma_probe.argtypes = [ci, ci, vp, vp]
     stp = ctypes.POINTER(SolStrides)
@@ -93,7 +95,8 @@ def load_library(path: str = LIB_PATH):
     lib.sol_proxy_map.argtypes = [shp, vp, vp, ci, vp, vp, sz, vp]
     lib.sol_select_topk.argtypes = [shp, ci, vp, ctypes.c_int64, vp, vp]
     lib.sol_select_topp.argtypes = [shp, ci, vp, cf, vp, vp]
-    for f in ("sol_pool_kv", "sol_attn_fwd", "sol_attn_fwd_ex", "sol_dense_fwd", "sol_mfma_probe",
+    for f in ("sol_pool_kv", "sol_attn_fwd", "sol_attn_fwd_ex", "sol_attn_fwd_noalloc",
+              "sol_dense_fwd", "sol_mfma_probe",
               "sol_attn_fwd_masked", "sol_proxy_map", "sol_select_topk", "sol_select_topp",
               "sol_attn_fwd_strided", "sol_dense_fwd_strided"):
         getattr(lib, f).restype = ci
@@ -237,6 +240,23 @@ def attn_fwd(q, k, v, beta: float, block: int, out=None, workspace=None, debug: 
                                float(beta), block, _dev(out, "out"), _dev(workspace, "workspace"),
                                workspace.numel(), ctypes.byref(dstruct), _stream(stream)))
     return out, dbg
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20  # SOL_NOALLOC_SCRATCH_BYTES
+
+
+def attn_fwd_noalloc(q, k, v, beta: float, block: int, out, stream=None):
+    """sol_attn_fwd_noalloc: the forward pass with the library's own device scratch (no workspace
+    argument, nothing allocated by the call).  q, k, v, out: contiguous bf16 [B, H, N, d]."""
+    import torch
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        if t.shape != q.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous bf16 with the shape of q")
+    _check(lib.sol_attn_fwd_noalloc(ctypes.byref(_shape(q)), _dev(q, "q"), _dev(k, "k"),
+                                    _dev(v, "v"), float(beta), block, _dev(out, "out"),
+                                    _stream(stream)))
+    return out
 
 
 def dense_fwd(q, k, v, out=None, want_lse: bool = False, stream=None):

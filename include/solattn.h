@@ -193,6 +193,25 @@ int sol_attn_fwd_masked(const sol_shape* shape, const void* q, const void* k, co
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sol_attn_fwd without a caller workspace, for callers that cannot allocate device memory (code
+ * under stream capture, tight serving loops, harnesses that forbid allocation).  Arguments,
+ * result and errors as for sol_attn_fwd; q, k, v, out contiguous [B][H][N][d] bf16, owned by the
+ * caller.  The workspace is a library-owned device array of SOL_NOALLOC_SCRATCH_BYTES per GPU,
+ * reserved when the library's kernels are loaded on that GPU and held until the process ends; the
+ * call itself allocates and frees nothing.  Heads are independent, so they run in the largest
+ * groups whose workspace (sol_attn_workspace_bytes for those heads) fits the array, one group
+ * after another on `stream`; the output is that of sol_attn_fwd up to the order in which a row's
+ * kept blocks are summed.  SOL_EWORKSPACE when a single head needs more than the array holds
+ * (sol_attn_workspace_bytes of a one-head shape); nothing is launched then.
+ * Every call on one GPU shares that GPU's array (each kernel writes what it later reads, so no
+ * contents carry over from a previous call): calls that may overlap in time on one GPU -- on
+ * different streams, or from several threads -- race and must be serialised by the caller.
+ */
+#define SOL_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int sol_attn_fwd_noalloc(const sol_shape* shape, const void* q, const void* k, const void* v,
+                         float beta, int block, void* out, void* stream);
+
+/*
  * Matrix-core rate probe (measurement only, not part of the attention path): `workgroups`
  * workgroups of 4 waves each issue iters x 8 independent bf16 32x32x16 MFMAs (32768 FLOPs each)
  * on register operands, so FLOPs = workgroups * 4 * iters * 8 * 32768.  sink (device,

@@ -123,6 +123,54 @@ def test_attn_fwd_rejects(lib, case):
     assert lib.sol_last_error(), case
 
 
+@pytest.mark.parametrize("case", ["null_shape", "null_q", "null_out", "misaligned_v", "nan_beta",
+                                  "bad_d", "bad_block", "zero_n", "out_overlaps_k",
+                                  "head_exceeds_scratch"])
+def test_attn_fwd_noalloc_rejects(lib, case):
+    """The allocation-free call validates everything, including whether one head's workspace fits
+    its scratch (SOL_NOALLOC_SCRATCH_BYTES), before its first HIP call."""
+    s = _shape()
+    q, k, v, out = _ptrs(4)
+    beta, block = 0.5, 128
+    expect = solattn.SOL_EINVAL
+    shape_arg = ctypes.byref(s)
+    if case == "null_shape":
+        shape_arg = None
+    elif case == "null_q":
+        q = None
+    elif case == "null_out":
+        out = None
+    elif case == "misaligned_v":
+        v = ctypes.c_void_p(v.value + 2)
+    elif case == "nan_beta":
+        beta = float("nan")
+    elif case == "bad_d":
+        s.d = 256
+        expect = solattn.SOL_EUNSUPPORTED
+    elif case == "bad_block":
+        block = 96
+        expect = solattn.SOL_EUNSUPPORTED
+    elif case == "zero_n":
+        s.N = 0
+    elif case == "out_overlaps_k":
+        out = ctypes.c_void_p(k.value + 256)
+    elif case == "head_exceeds_scratch":
+        # 2^21 tokens in 64-key blocks: 1024 selection words per row, 8 GiB of them per head
+        s.N, s.H, block = 1 << 21, 1, 64
+        one = solattn.SolShape(1, 1, s.N, s.d)
+        assert lib.sol_attn_workspace_bytes(ctypes.byref(one), block) > solattn.NOALLOC_SCRATCH_BYTES
+        expect = solattn.SOL_EWORKSPACE
+    st = lib.sol_attn_fwd_noalloc(shape_arg, q, k, v, beta, block, out, None)
+    assert st == expect, (case, st, lib.sol_last_error())
+    assert lib.sol_last_error(), case
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define SOL_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == solattn.NOALLOC_SCRATCH_BYTES
+
+
 def test_infinite_beta_passes_validation_only_to_workspace_check(lib):
     """+-inf beta are valid values: with an undersized workspace the call fails on the workspace,
     not on beta."""
