@@ -167,6 +167,7 @@ const char* sol_status_str(int status) {
     case SOL_EUNSUPPORTED: return "unsupported head dimension or block size";
     case SOL_EWORKSPACE: return "workspace missing or too small";
     case SOL_EHIP: return "HIP runtime error";
+    case SOL_ENOTIMPL: return "not implemented";
     default: return "unknown status";
   }
 }

@@ -1907,9 +1907,9 @@ static hipError_t launch_sparse_t(const SparseArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Four waves per workgroup and two workgroups per CU: measured at the Wan2.1-14B shape, eight
-// waves (one workgroup per CU, each copy shared by twice the rows) were 9% slower -- the second
-// workgroup's independent progress is worth more than the halved copy traffic.
+// The 16-row kernel: eight waves of 16 rows per 128-row tile, two workgroups per CU (four waves
+// per SIMD).  Dynamic LDS: the stage / routing-chunk region, the waves' union words and the
+// 4-slot stage descriptor ring.
 template <int D, int BLK>
 static hipError_t launch_sparse16_t(const SparseArgs& a, hipStream_t stream) {
   const size_t smem = sparse_smem_bytes(D, a.Mp, 0) + (size_t)kWaves16 * (a.Mp / 32) * 4 + 4 * 4;

@@ -18,6 +18,7 @@ SOL_EINVAL = -1
 SOL_EUNSUPPORTED = -2
 SOL_EWORKSPACE = -3
 SOL_EHIP = -4
+SOL_ENOTIMPL = -5
 QUERY_TILE = 128
 
 # Every symbol include/solattn.h declares.

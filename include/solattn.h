@@ -49,7 +49,8 @@ typedef enum sol_status {
   SOL_EINVAL = -1,        /* NULL/misaligned pointer, bad size, NaN beta */
   SOL_EUNSUPPORTED = -2,  /* d or block outside the supported set */
   SOL_EWORKSPACE = -3,    /* workspace NULL or smaller than sol_attn_workspace_bytes() */
-  SOL_EHIP = -4           /* the HIP runtime reported an error at launch */
+  SOL_EHIP = -4,          /* the HIP runtime reported an error at launch */
+  SOL_ENOTIMPL = -5       /* reserved: no call of this version returns it */
 } sol_status;
 
 /* Tensor extents: batch, heads, tokens, head dimension. */
@@ -133,8 +134,11 @@ int sol_attn_fwd_strided(const sol_shape* shape, const sol_strides* in_strides,
                          size_t workspace_bytes, void* stream);
 
 /*
- * Dense reference attention: out = softmax(q k^T / sqrt(d)) v over all N keys, no mask.  The
- * speedup of the sparse pass is measured against this.
+ * Dense reference attention: out = softmax(q k^T / sqrt(d)) v over all N keys, no mask
+ * (bidirectional, as the page's limitations paragraph states).  The page measures Sol-Attn against
+ * dense FlashAttention (paragraph on the results: the kernel-level speedup on H100 and the LTX
+ * table); this is the library's own dense kernel in that role, and the speedup of the sparse pass
+ * is measured against it on the same tensors.
  *   q, k, v, out  [B][H][N][d] bf16, device.   lse  [B][H][N] fp32, device, or NULL.
  */
 int sol_dense_fwd(const sol_shape* shape, const void* q, const void* k, const void* v, void* out,

@@ -47,7 +47,7 @@ def test_exported_symbols_are_c_names():
 
 def test_version_and_status_strings(lib):
     assert b"gfx950" in lib.sol_version()
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         assert lib.sol_status_str(st)
     assert lib.sol_status_str(99) == b"unknown status"
 
