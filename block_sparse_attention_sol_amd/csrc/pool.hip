@@ -4,11 +4,11 @@
 // score of the Sol-Attn page's routing paragraph is q . Kbar_j / sqrt(d), and Vbar_j is the value
 // of block j's pooled token.
 //
-// One workgroup pools one key block of one (batch, head) for both K and V: 256 threads read the
-// block's rows as 16-byte chunks (consecutive threads -> consecutive chunks of a row, so each
-// load instruction covers whole rows), accumulate fp32 partial sums over a strided subset of rows,
-// then combine the partials through LDS in a fixed order (deterministic).  Besides the fp32
-// means it writes the layouts the attention kernel consumes:
+// One workgroup pools 32 consecutive key blocks of one (batch, head) for both K and V: each wave
+// reads its blocks' rows as 16-byte chunks (consecutive lanes -> consecutive chunks of a row, so
+// each load instruction covers whole rows), accumulates fp32 sums and combines the lanes sharing a
+// chunk with cross-lane operations in a fixed order (deterministic).  Besides the fp32 means it
+// writes the layouts the attention kernel consumes:
 //   kp   [3][BH][Mp][d] bf16: Kbar split into hi + mid + lo bf16 pieces whose sum is the fp32
 //        value, so a bf16 matrix product over the three pieces reproduces fp32 proxies;
 //   vbt  [BH][d][Mp] bf16: Vbar transposed (block index contiguous), the A operand of the
@@ -22,79 +22,135 @@
 
 namespace solattn {
 
+constexpr int kPoolWaves = 8;                // waves per pooling workgroup
+constexpr int kPoolBlocks = 32;              // key blocks per pooling workgroup
+constexpr int kPoolPerWave = kPoolBlocks / kPoolWaves;
+
+// Sum of x over the lanes that hold the same 16-byte chunk of a row: lanes l, l + C, l + 2C, ...
+// for C = D / 8 chunks per row (D = 128: four lanes, D = 64: eight), every lane receiving the sum.
+// DPP within a 16-lane row, then the permlane swaps of the 16x16 layout helpers.
 template <int D>
-__global__ __launch_bounds__(kThreads) void pool_kv_kernel(
+__device__ __forceinline__ float chunk_sum(float x) {
+  if constexpr (D == 64)
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128,
+                                                               0xF, 0xF, false));  // row_ror:8
+  return quad_sum(x);
+}
+
+// One workgroup pools kPoolBlocks consecutive key blocks of one (batch, head), for K and V; each
+// wave takes kPoolPerWave of them.  A wave loads whole rows (lane l: 16-byte chunk l % C of rows
+// l / C, l / C + 64 / C, ...), keeps fp32 sums of its chunk, and combines the lanes that share a
+// chunk with cross-lane operations (fixed order: deterministic).  The mean divides by n_j.  Vbar^T
+// is staged in LDS and written as one 2 x kPoolBlocks-byte run per head-dimension row.
+template <int D>
+__global__ __launch_bounds__(64 * kPoolWaves) void pool_kv_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, Strides kv, int64_t N, int block,
     int64_t M, int64_t Mp, float* __restrict__ kbar, float* __restrict__ vbar,
     uint16_t* __restrict__ kp, uint16_t* __restrict__ vbt) {
-  constexpr int kChunks = D / 8;               // 16-byte chunks per row
-  constexpr int kGroups = kThreads / kChunks;  // row groups
-  __shared__ float part[2][kGroups][D];
-
-  const int64_t j = blockIdx.x;
+  constexpr int C = D / 8;           // 16-byte chunks per row
+  constexpr int RS = 64 / C;         // rows per wave load instruction
+  constexpr int U = 8;               // row sets in flight per tensor
+  __shared__ __attribute__((aligned(16))) uint16_t vt[D][kPoolBlocks];
   const int64_t bh = blockIdx.y;
-  const int t = threadIdx.x;
-  const int cc = t % kChunks;
-  const int rg = t / kChunks;
-
-  if (j >= M) {  // padding block of the split layouts
-    if (t < D) {
-      if (kp) {
-        for (int p = 0; p < 3; ++p) kp[((p * gridDim.y + bh) * Mp + j) * D + t] = 0;
-      }
-      if (vbt) vbt[(bh * D + t) * Mp + j] = 0;
-    }
-    return;
-  }
-
-  const int64_t lo = j * (int64_t)block;
-  const int64_t hi = (lo + block < N) ? lo + block : N;
+  const int64_t BH = gridDim.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cc = lane % C, rs = lane / C;
   const uint16_t* kb = k + kv.base(bh);
   const uint16_t* vb = v + kv.base(bh);
-
-  float sk[8], sv[8];
+  const int64_t jlast = (kp || vbt) ? Mp : M;  // blocks written (padding blocks: zeros)
+  for (int bl = 0; bl < kPoolPerWave; ++bl) {
+    const int jl = wave * kPoolPerWave + bl;  // block within the group
+    const int64_t j = (int64_t)blockIdx.x * kPoolBlocks + jl;
+    if (j >= jlast) break;
+    float sk[8], sv[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) sk[e] = sv[e] = 0.f;
-  for (int64_t r = lo + rg; r < hi; r += kGroups) {
-    u32x4 a = *reinterpret_cast<const u32x4*>(kb + r * kv.sn + cc * 8);
-    u32x4 b = *reinterpret_cast<const u32x4*>(vb + r * kv.sn + cc * 8);
+    for (int e = 0; e < 8; ++e) sk[e] = sv[e] = 0.f;
+    const int64_t lo = j * (int64_t)block;
+    const int64_t hi = lo + block < N ? lo + block : N;
+    if (j < M) {
+      for (int64_t r0 = lo; r0 < hi; r0 += RS * U) {
+        u32x4 a[U], b[U];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sk[2 * e] += bf16_lo(a[e]);
-      sk[2 * e + 1] += bf16_hi(a[e]);
-      sv[2 * e] += bf16_lo(b[e]);
-      sv[2 * e + 1] += bf16_hi(b[e]);
+        for (int u = 0; u < U; ++u) {
+          const int64_t r = r0 + u * RS + rs;
+          a[u] = b[u] = u32x4{0u, 0u, 0u, 0u};
+          if (r < hi) {
+            a[u] = *reinterpret_cast<const u32x4*>(kb + r * kv.sn + cc * 8);
+            b[u] = *reinterpret_cast<const u32x4*>(vb + r * kv.sn + cc * 8);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sk[2 * e] += bf16_lo(a[u][e]);
+            sk[2 * e + 1] += bf16_hi(a[u][e]);
+            sv[2 * e] += bf16_lo(b[u][e]);
+            sv[2 * e + 1] += bf16_hi(b[u][e]);
+          }
+      }
+    }
+    float mk[8], mv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // true division by n_j (the reciprocal is not used: n_j need not be a power of two)
+      mk[e] = j < M ? chunk_sum<D>(sk[e]) / (float)(hi - lo) : 0.f;
+      mv[e] = j < M ? chunk_sum<D>(sv[e]) / (float)(hi - lo) : 0.f;
+    }
+    if (rs == 0) {  // lanes 0 .. C - 1 hold the block's means at d = 8 cc .. 8 cc + 7
+      if (j < M) {
+        if (kbar) {
+          float* kr = kbar + (bh * M + j) * D + cc * 8;
+          *reinterpret_cast<f32x4*>(kr) = f32x4{mk[0], mk[1], mk[2], mk[3]};
+          *reinterpret_cast<f32x4*>(kr + 4) = f32x4{mk[4], mk[5], mk[6], mk[7]};
+        }
+        if (vbar) {
+          float* vr = vbar + (bh * M + j) * D + cc * 8;
+          *reinterpret_cast<f32x4*>(vr) = f32x4{mv[0], mv[1], mv[2], mv[3]};
+          *reinterpret_cast<f32x4*>(vr + 4) = f32x4{mv[4], mv[5], mv[6], mv[7]};
+        }
+      }
+      if (kp) {
+        u32x4 ph, pm, pl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t h2[2], m2[2], l2[2];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const float m = mk[2 * e + x];
+            const uint16_t h16 = f32_to_bf16_rne(m);
+            const float r1 = m - bits_f32((uint32_t)h16 << 16);
+            const uint16_t m16 = f32_to_bf16_rne(r1);
+            const uint16_t l16 = f32_to_bf16_rne(r1 - bits_f32((uint32_t)m16 << 16));
+            h2[x] = h16;
+            m2[x] = m16;
+            l2[x] = l16;
+          }
+          ph[e] = h2[0] | (h2[1] << 16);
+          pm[e] = m2[0] | (m2[1] << 16);
+          pl[e] = l2[0] | (l2[1] << 16);
+        }
+        const int64_t off = (bh * Mp + j) * D + cc * 8;
+        *reinterpret_cast<u32x4*>(kp + off) = ph;
+        *reinterpret_cast<u32x4*>(kp + BH * Mp * D + off) = pm;
+        *reinterpret_cast<u32x4*>(kp + 2 * BH * Mp * D + off) = pl;
+      }
+      if (vbt) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vt[cc * 8 + e][jl] = f32_to_bf16_rne(mv[e]);
+      }
     }
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    part[0][rg][cc * 8 + e] = sk[e];
-    part[1][rg][cc * 8 + e] = sv[e];
-  }
-  __syncthreads();
-
-  if (t < 2 * D) {
-    const int which = t / D;  // 0: K, 1: V
-    const int c = t % D;
-    float s = 0.f;
-    for (int g = 0; g < kGroups; ++g) s += part[which][g][c];
-    const float mean = s / (float)(hi - lo);
-    if (which == 0) {
-      if (kbar) kbar[(bh * M + j) * D + c] = mean;
-      if (kp) {
-        const uint16_t h16 = f32_to_bf16_rne(mean);
-        const float r1 = mean - bits_f32((uint32_t)h16 << 16);
-        const uint16_t m16 = f32_to_bf16_rne(r1);
-        const float r2 = r1 - bits_f32((uint32_t)m16 << 16);
-        const uint16_t l16 = f32_to_bf16_rne(r2);
-        const int64_t BH = gridDim.y;
-        kp[((0 * BH + bh) * Mp + j) * D + c] = h16;
-        kp[((1 * BH + bh) * Mp + j) * D + c] = m16;
-        kp[((2 * BH + bh) * Mp + j) * D + c] = l16;
-      }
-    } else {
-      if (vbar) vbar[(bh * M + j) * D + c] = mean;
-      if (vbt) vbt[(bh * D + c) * Mp + j] = f32_to_bf16_rne(mean);
+  if (vbt) {
+    __syncthreads();
+    // row d of the group's Vbar^T tile: kPoolBlocks bf16 = 4 chunks of 16 bytes
+    const int64_t j0 = (int64_t)blockIdx.x * kPoolBlocks;
+    for (int i = threadIdx.x; i < D * (kPoolBlocks / 8); i += 64 * kPoolWaves) {
+      const int d = i / (kPoolBlocks / 8), ch = i % (kPoolBlocks / 8);
+      if (j0 + ch * 8 < Mp)
+        *reinterpret_cast<u32x4*>(vbt + (bh * D + d) * Mp + j0 + ch * 8) =
+            *reinterpret_cast<const u32x4*>(&vt[d][ch * 8]);
     }
   }
 }
@@ -294,14 +350,14 @@ hipError_t launch_pool(int d, int64_t BH, int64_t N, int block, const void* k, c
                        float* kbar, float* vbar, uint16_t* kp, uint16_t* vbt, int64_t Mp,
                        hipStream_t stream) {
   const int64_t M = (N + block - 1) / block;
-  const int64_t gx = (kp || vbt) ? Mp : M;
-  dim3 grid((unsigned)gx, (unsigned)BH);
+  const int64_t nb = (kp || vbt) ? Mp : M;
+  dim3 grid((unsigned)((nb + kPoolBlocks - 1) / kPoolBlocks), (unsigned)BH);
   if (d == 64)
-    hipLaunchKernelGGL(pool_kv_kernel<64>, grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL(pool_kv_kernel<64>, grid, dim3(64 * kPoolWaves), 0, stream,
                        (const uint16_t*)k, (const uint16_t*)v, kv, N, block, M, Mp, kbar, vbar, kp,
                        vbt);
   else
-    hipLaunchKernelGGL(pool_kv_kernel<128>, grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL(pool_kv_kernel<128>, grid, dim3(64 * kPoolWaves), 0, stream,
                        (const uint16_t*)k, (const uint16_t*)v, kv, N, block, M, Mp, kbar, vbar, kp,
                        vbt);
   return hipGetLastError();
