@@ -277,6 +277,10 @@ def routing_comparison(sol, w, q, k, v, ws, spec, steps=5, warmup=2):
     }
 
 
+# the fused kernels' sources: a counter record stays valid while these are unchanged
+FUSED_SOURCES = ("attn.hip", "tiles.hpp", "common.hpp", "kernels.hpp")
+
+
 def recorded_traffic(kernel_sources, workload, beta):
     """HBM bytes per launch of the fused kernel, as recorded from rocprofv3 FETCH_SIZE/WRITE_SIZE
     counters (scaled by a plain-copy calibration) in profiles/sol_attn_wan_hbm_traffic.md, or
@@ -464,7 +468,7 @@ def main():
     min_bytes = 4.0 * B * H * N * d * 2
     traffic = recorded_traffic(
         [os.path.join(ROOT, "block_sparse_attention_sol_amd", "csrc", f)
-         for f in ("attn.hip", "common.hpp", "kernels.hpp")], w.name, beta)
+         for f in FUSED_SOURCES], w.name, beta)
     result = {
         "metric": METRIC,
         "value": F_tile / (t_sparse * 1e-3) / 1e12,

@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsolattn.so")
-SOURCES = ["api.cpp", "pool.hip", "attn.hip", "route.hip", "probe.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "pool.hip", "stats.hip", "attn.hip", "dense.hip", "route.hip", "probe.hip",
+           "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -1,5 +1,4 @@
-// attn.hip -- row statistics, the fused Sol-Attn forward kernel and the dense reference kernel
-// (gfx950).
+// attn.hip -- the fused Sol-Attn forward kernels (gfx950).
 //
 // Method (page "Sol-Attn: Accelerating Video Generation Inference via On-the-Fly Attention
 // Sparsification", agihunt.info/papers/2607.24027): per query, a proxy score for every key block,
@@ -10,14 +9,6 @@
 // block with logit s + ln(n_blk) and value mean(V_blk).
 //
 // Kernels
-//   rowstats_kernel  mu_i = q_i . g / sqrt(d) and sigma_i^2 = q_i^T C q_i / d, where g and C are the
-//                    mean and covariance of the pooled keys: the mean and population variance of
-//                    the proxy row, exactly, without visiting its M entries.  mu in fp64.  C q is
-//                    one bf16 matrix product per 32 rows over the hi + mid + lo pieces of C
-//                    (fp32-accurate), after C's dominant directions, if any, are split off and
-//                    taken in fp64 (see the pooled-key statistics).
-//                    Writes tau_i = mu_i + beta * sigma_i (-inf for the fused kernel where
-//                    sigma_i = 0: every proxy of such a row equals tau, so it keeps every block).
 //   sol_attn_kernel  (head dimension 64) one workgroup = 4 waves = 128 query rows of one
 //                    (batch, head); each wave owns
 //                    32 rows, one row per lane pair (lanes c and c + 32).  Scores are computed
@@ -44,761 +35,10 @@
 //                    and publishes each stage as a word in an LDS ring, and the lowest wave
 //                    without math issues the whole next-stage copy.  Each tile's walk starts at
 //                    a point that lines up the tiles running together on an XCD.
-//   dense_attn_kernel the exact loop over every key: the reference the speedup is measured against.
 // The proxy map is never written to memory; only the optional debug outputs leave the kernel.
-#include <math.h>
-
-#include "common.hpp"
-#include "kernels.hpp"
+#include "tiles.hpp"
 
 namespace solattn {
-
-namespace {
-
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kStage = 64;  // keys per pipeline stage
-// Row statistics: eight waves of 32 rows share the staged covariance pieces (two waves per SIMD
-// hide each other's latency; the pieces' 96 KB of LDS at d = 128 allow one workgroup per CU),
-// over kRowStatsPasses passes of 256 rows.
-constexpr int kRowStatsWaves = 8;
-constexpr int kRowStatsThreads = 64 * kRowStatsWaves;
-constexpr int kRowStatsRows = 32 * kRowStatsWaves;  // rows per pass
-constexpr int kRowStatsPasses = 8;
-
-// ---------------------------------------------------------------------------------------------
-// LDS tiles: row-major [rows][D] bf16, 16-byte chunks XOR-swizzled per row.  The swizzle makes
-// the access patterns conflict-free on a 256-byte-wide LDS: 16 consecutive rows read at one
-// logical chunk (the K / Kbar A operand) land on 16 distinct 16-byte bank groups, and the
-// transpose reads of V land on distinct chunks per 32 lanes -- 4 consecutive rows x 4 adjacent
-// chunks (32x32 layout), or two 4-row groups x 2 chunks (16x16 layout, where bit 2 of the row
-// goes to chunk bit 1 so that the two groups differ in a bit the read does not cover).
-// ---------------------------------------------------------------------------------------------
-template <int D>
-__device__ __forceinline__ int swz(int row, int ch) {
-  if constexpr (D == 128)
-    return ch ^ (((row & 3) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1));
-  else return ch ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
-}
-// Pooled-key chunk tiles of the 16-row kernel (D = 128, 32 rows): the proxy reads take rows in
-// the order 8 (q / 4) + 4 bt + q % 4 for lane q and block tile bt (so that lane row g's scores are
-// blocks 8g .. 8g + 7), which leaves row bit 2 fixed across the 16 lanes of a read; the swizzle
-// takes row bits 0, 1, 3 and 4, distinct for those 16 rows.
-__device__ __forceinline__ int swz_pk(int row, int ch) {
-  return ch ^ (((row & 3) << 2) | ((row >> 3) & 3));
-}
-template <int D>
-__device__ __forceinline__ int tile_off(int row, int ch) {  // byte offset of a 16-byte chunk
-  return row * (2 * D) + (swz<D>(row, ch) << 4);
-}
-
-// Copy rows [row0, row0 + ROWS) of a row-major [*, D] bf16 matrix into an LDS tile with
-// global_load_lds (16 bytes per lane, no registers).  Rows >= limit read row limit - 1 instead
-// (finite data; such keys are masked).  Every thread of an NT-thread workgroup issues
-// ROWS * D / 8 / NT loads.
-template <int D, int ROWS, int NT = kThreads>
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ src, int64_t row0,
-                                          int64_t limit, lds_u8* tile) {
-  constexpr int kChunks = D / 8;
-  constexpr int kIters = ROWS * kChunks / NT;
-  static_assert(ROWS * kChunks % NT == 0, "tile must split into whole wave loads");
-  const int t = threadIdx.x;
-  const int wave = t >> 6;
-#pragma unroll
-  for (int i = 0; i < kIters; ++i) {
-    const int p = i * NT + t;  // physical slot written by this lane
-    const int row = p / kChunks;
-    const int ch = swz<D>(row, p % kChunks);  // logical chunk stored in that slot (XOR involution)
-    int64_t grow = row0 + row;
-    if (grow >= limit) grow = limit - 1;
-    const uint16_t* g = src + grow * D + ch * 8;
-    lds_u8* dst = tile + (i * NT + wave * 64) * 16;  // wave-uniform; lane l lands at +16 l
-    __builtin_amdgcn_global_load_lds((const void*)g, (__attribute__((address_space(3))) void*)dst,
-                                     16, 0, 0);
-  }
-}
-template <int D, int ROWS, int NT = kThreads>
-constexpr int tile_loads() { return ROWS * (D / 8) / NT; }
-
-// Buffer resource descriptor over `bytes` bytes at `base` (raw buffer: stride 0, 32-bit dword
-// data format): loads past `bytes` return zeros.  Built from wave-uniform values, so it lives in
-// scalar registers.
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t addr = (uint64_t)(uintptr_t)base;
-  i32x4_t r;
-  r[0] = (int)__builtin_amdgcn_readfirstlane((uint32_t)addr);
-  r[1] = (int)__builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32) & 0xffffu);
-  r[2] = (int)__builtin_amdgcn_readfirstlane(bytes);
-  r[3] = 0x00020000;
-  return r;
-}
-
-// Per-lane byte offsets, within a ROWS-row tile of a bf16 matrix with rows of D contiguous
-// elements sn elements apart, of the 16 bytes each lane copies so that the LDS tile comes out
-// swizzled (see load_tile).
-// PK: the pooled-key tile swizzle (swz_pk) instead of swz.
-template <int D, int ROWS, int NT = kThreads, bool PK = false>
-struct TileOffsets {
-  static_assert(!PK || D == 128, "the pooled-key swizzle covers 16 chunks per row");
-  uint32_t v[tile_loads<D, ROWS, NT>()];
-  __device__ __forceinline__ explicit TileOffsets(int64_t sn, int tid = (int)threadIdx.x) {
-    constexpr int kChunks = D / 8;
-#pragma unroll
-    for (int i = 0; i < tile_loads<D, ROWS, NT>(); ++i) {
-      const int p = i * NT + tid;
-      const int row = p / kChunks;
-      const int ch = PK ? swz_pk(row, p % kChunks) : swz<D>(row, p % kChunks);
-      v[i] = (uint32_t)(row * sn * 2 + ch * 16);
-    }
-  }
-};
-
-// Copy the first ROWS rows of the buffer `rsrc` into LDS with buffer loads (16 bytes per lane,
-// straight to LDS).  Rows past the buffer end read as zeros: the range check covers the per-lane
-// offset, so callers start the resource at the tile (soff stays 0; a scalar offset would bypass
-// the check).
-//
-// The copy is issued as an asm statement rather than through the compiler's LDS-DMA builtin: the
-// compiler cannot tell which LDS buffer such a copy writes, and would make every LDS transpose
-// read wait for all copies in flight -- including the next stage's prefetch, serialising copy and
-// math.  The instruction has no register result (its destination is LDS), its address operands
-// are consumed at issue, and the callers order the LDS traffic themselves: wait_vmcnt before the
-// barrier that publishes a tile, and a barrier before a buffer is refilled.
-// One copy of 16 bytes per lane from the buffer `rsrc` (at byte voff + soff) to LDS; lane l lands
-// at dst + 16 l, dst wave-uniform.  The LDS destination base goes in m0 as an operand bound to
-// that register, so the compiler sets m0 itself (one scalar move; it knows m0's value afterwards)
-// and knows this statement writes LDS.  These copies sit in every stage's scalar-bound
-// bookkeeping, where a save and restore of m0 around each would cost two more scalar
-// instructions per copy.
-__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t soff, lds_u8* dst) {
-  __asm__ __volatile__("buffer_load_dwordx4 %[voff], %[rsrc], %[soff] offen lds"
-                       :
-                       : "{m0}"(dst), [voff] "v"(voff), [rsrc] "s"(rsrc), [soff] "s"(soff)
-                       : "memory");
-}
-
-template <int D, int ROWS, int NT = kThreads, bool PK = false>
-__device__ __forceinline__ void load_tile_buf(i32x4_t rsrc, uint32_t soff,
-                                              const TileOffsets<D, ROWS, NT, PK>& off, lds_u8* tile) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-  for (int i = 0; i < tile_loads<D, ROWS, NT>(); ++i)
-    dma16(rsrc, off.v[i], soff, tile + (i * NT + wave * 64) * 16);
-}
-
-// Rows [row0, row0 + ROWS) of a row-major [*, D] bf16 matrix whose rows all exist (pooled-key
-// pieces, padded to Mp rows), copied as load_tile does but without the compiler's LDS-DMA builtin
-// (see load_tile_buf): a builtin copy in flight makes the compiler wait for every outstanding
-// memory operation before the next LDS write, which stalls the routing sweep once per chunk.
-template <int D, int ROWS, int NT = kThreads, bool PK = false>
-__device__ __forceinline__ void load_dense_rows(const uint16_t* src, int64_t row0,
-                                                const TileOffsets<D, ROWS, NT, PK>& off, lds_u8* tile) {
-  load_tile_buf<D, ROWS, NT, PK>(make_rsrc(src + row0 * D, ROWS * D * 2), 0u, off, tile);
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-// s_waitcnt lgkmcnt(0) alone (gfx9 encoding: vmcnt and expcnt left at their maxima).
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
-
-// Rows [r0, r0 + ROWS) of a row-strided bf16 matrix (row r at base + r * sn, rows below `limit`)
-// into an LDS tile; rows at or beyond `limit` read as zeros (the buffer ends after the last valid
-// row, and every later row starts at or beyond that end since sn >= D).  The buffer covers all
-// the remaining valid rows, not just this tile's: measured on gfx950, a resource cut to the tile
-// made the dense loop fetch 3.7x more bytes from beyond L2.
-template <int D, int ROWS, int NT = kThreads>
-__device__ __forceinline__ void load_rows(const uint16_t* base, int64_t r0, int64_t limit, int64_t sn,
-                                          const TileOffsets<D, ROWS, NT>& off, lds_u8* tile) {
-  const int64_t rest = (limit - r0 - 1) * sn * 2 + D * 2;
-  const uint32_t bytes = (uint32_t)(rest < 0xffffffffll ? rest : 0xffffffffll);
-  load_tile_buf<D, ROWS, NT>(make_rsrc(base + r0 * sn, bytes), 0u, off, tile);
-}
-
-// Share k of the copy load_rows makes of rows [r0, r0 + ROWS) (the loads lane l of wave k issues
-// there), issued by the calling wave instead; k is wave-uniform.  rsrc starts at row r0 and ends
-// after the head's last valid row (load_rows' range); sn2 is the row stride in bytes.
-template <int D, int ROWS, int NT>
-__device__ __forceinline__ void copy_share(i32x4_t rsrc, uint32_t sn2, int k, int lane,
-                                           lds_u8* tile) {
-  constexpr int kChunks = D / 8;
-  static_assert(64 % kChunks == 0 && NT % kChunks == 0, "a wave's slots cover whole rows");
-  // The offsets TileOffsets would give, split into a wave-uniform and a per-lane part: slot
-  // i NT + 64 k + lane holds row rs + rl (rs = (i NT + 64 k) / kChunks, a multiple of
-  // 64 / kChunks, and rl = lane / kChunks < 64 / kChunks) and logical chunk
-  // (lane % kChunks) ^ f(rs + rl).  The swizzle f only permutes row bits, so
-  // f(rs + rl) = f(rs) ^ f(rl).
-  const int rl = lane / kChunks;
-  const uint32_t lane_row = (uint32_t)rl * sn2;
-  const int cl = swz<D>(rl, lane % kChunks);
-#pragma unroll
-  for (int i = 0; i < tile_loads<D, ROWS, NT>(); ++i) {
-    const int rs = (i * NT + 64 * k) / kChunks;  // wave-uniform
-    const uint32_t voff = (uint32_t)rs * sn2 + lane_row + ((uint32_t)(cl ^ swz<D>(rs, 0)) << 4);
-    dma16(rsrc, voff, 0u, tile + (i * NT + k * 64) * 16);
-  }
-}
-
-// Workgroup barrier without the memory fence of __syncthreads: the pipelined loops order their
-// LDS traffic themselves (explicit vmcnt waits for the LDS-bound copies; LDS reads are consumed
-// before the barrier), so the fence's wait for every outstanding load -- including the next
-// stage's prefetch -- is not wanted.  The empty asm statements keep the compiler from moving
-// memory accesses across it.
-__device__ __forceinline__ void bar() {
-  __asm__ __volatile__("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  __asm__ __volatile__("" ::: "memory");
-}
-
-__device__ __forceinline__ u32x4 lds_read16(const lds_u8* p) {
-  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
-}
-
-// ---------------------------------------------------------------------------------------------
-// Per-wave tile math
-// ---------------------------------------------------------------------------------------------
-
-// S^T (32 keys = tile rows kr0 .. kr0 + 31) x (this lane's query): D/16 MFMAs.
-template <int D>
-__device__ __forceinline__ f32x16 scores32(const lds_u8* tile, int kr0, const bf16x8 (&qf)[D / 16],
-                                           f32x16 acc) {
-  const int lane = threadIdx.x & 63;
-  const int c = lane & 31, h = lane >> 5;
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    const u32x4 raw = lds_read16(tile + tile_off<D>(kr0 + c, 2 * kk + h));
-    acc = mfma32(__builtin_bit_cast(bf16x8, raw), qf[kk], acc);
-  }
-  return acc;
-}
-
-// The bf16 B operand holding probabilities 8*e2 .. 8*e2 + 7 of a 32-key score block, from the
-// 8 packed words of that block.
-__device__ __forceinline__ bf16x8 p_operand(const uint32_t* pk, int e2) {
-  u32x4 w;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) w[m] = pk[4 * e2 + m];
-  return __builtin_bit_cast(bf16x8, w);
-}
-
-// Round 16 probabilities to bf16 pairs (pk[8]) and add the rounded values to `sum`.
-__device__ __forceinline__ float round_p(const float* p, uint32_t* pk, float sum) {
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    pk[m] = pack_bf16x2(p[2 * m], p[2 * m + 1]);
-    sum = add_bf16x2(pk[m], sum);
-  }
-  return sum;
-}
-
-// O^T[ds] += V^T P^T for one 32-key score block (tile rows kr0 .. kr0 + 31 of a V tile).
-// Score register v of lane half h belongs to key 8*(v/4) + 4*h + v%4; the probabilities of
-// registers 8*e2 .. 8*e2 + 7 form the B operand of one MFMA, whose A operand (V^T restricted to
-// those 8 keys, this lane's d column) comes from two LDS transpose reads.  In each 16-lane group
-// the source lane j points at key row (e = j/4 of the 4 keys) and 4 columns (j%4); the hardware
-// hands lane i column i of each of the 4 rows.
-template <int D>
-__device__ __forceinline__ void pv32(const lds_u8* vtile, int kr0, const uint32_t* pk,
-                                     f32x16 (&o)[D / 32]) {
-  const int lane = threadIdx.x & 63;
-  const int grp = lane >> 4, j = lane & 15;
-  const int h = grp >> 1, cg = grp & 1;
-#pragma unroll
-  for (int e2 = 0; e2 < 2; ++e2) {
-    const bf16x8 b = p_operand(pk, e2);
-#pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds) {
-      const int d0 = 32 * ds + 16 * cg + 4 * (j & 3);
-      s16x4 x[2];
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int row = kr0 + 16 * e2 + 8 * r + 4 * h + (j >> 2);
-        const lds_u8* p = vtile + tile_off<D>(row, d0 >> 3) + ((d0 >> 2) & 1) * 8;
-        x[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(p));
-      }
-      u32x4 raw;
-      raw[0] = __builtin_bit_cast(u32x2, x[0])[0];
-      raw[1] = __builtin_bit_cast(u32x2, x[0])[1];
-      raw[2] = __builtin_bit_cast(u32x2, x[1])[0];
-      raw[3] = __builtin_bit_cast(u32x2, x[1])[1];
-      o[ds] = mfma32(__builtin_bit_cast(bf16x8, raw), b, o[ds]);
-    }
-  }
-}
-
-// Vbar^T chunk tile: D rows (head dimension) x 32 blocks, 64-byte rows of four 16-byte chunks,
-// chunk index XOR (row / 4) % 4 so that 16 consecutive rows read at one position are spread over
-// the banks.  Copied from vbt [D][Mp] (block index contiguous).
-template <int D>
-__device__ __forceinline__ int vbt_off(int row, int ch) { return row * 64 + ((ch ^ ((row >> 2) & 3)) << 4); }
-
-// Per-lane byte offsets of the Vbar^T chunk copy (relative to the chunk's first column): lane
-// slot p of the tile holds row p / 4, logical chunk (p % 4) XOR the row's swizzle.
-template <int D, int NT = kThreads>
-struct VbtOffsets {
-  static_assert(D * 4 % NT == 0, "tile must split into whole wave loads");
-  uint32_t v[D * 4 / NT];
-  __device__ __forceinline__ explicit VbtOffsets(int64_t Mp) {
-#pragma unroll
-    for (int i = 0; i < D * 4 / NT; ++i) {
-      const int p = i * NT + (int)threadIdx.x;
-      const int row = p >> 2;
-      const int ch = (p & 3) ^ ((row >> 2) & 3);
-      v[i] = (uint32_t)(((int64_t)row * Mp + ch * 8) * 2);
-    }
-  }
-};
-
-// The Vbar^T tile of chunk cb (blocks 32 cb .. 32 cb + 31) into LDS, with buffer loads issued from
-// asm (see load_dense_rows for why).
-template <int D, int NT = kThreads>
-__device__ __forceinline__ void load_vbt_buf(const uint16_t* vt, int64_t Mp, int cb,
-                                             const VbtOffsets<D, NT>& off, lds_u8* tile) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const i32x4_t rsrc = make_rsrc(vt + (int64_t)cb * 32, (uint32_t)(((D - 1) * Mp + 32) * 2));
-#pragma unroll
-  for (int i = 0; i < D * 4 / NT; ++i) dma16(rsrc, off.v[i], 0u, tile + (i * NT + wave * 64) * 16);
-}
-
-// O^T[ds] += Vbar^T P^T for the 32 pooled blocks of a chunk (probability registers as in pv32).
-// The A operand for blocks {16 e2 + 4 h + 0..3} and {16 e2 + 8 + 4 h + 0..3} of this lane's d row
-// is two 8-byte reads of the transposed tile.
-template <int D>
-__device__ __forceinline__ void pv_pooled(const lds_u8* vt, const uint32_t* pk, f32x16 (&o)[D / 32]) {
-  const int lane = threadIdx.x & 63;
-  const int c = lane & 31, h = lane >> 5;
-#pragma unroll
-  for (int e2 = 0; e2 < 2; ++e2) {
-    const bf16x8 b = p_operand(pk, e2);
-#pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds) {
-      const int row = 32 * ds + c;
-      const u32x2 x0 = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
-          vt + vbt_off<D>(row, 2 * e2) + 8 * h);
-      const u32x2 x1 = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
-          vt + vbt_off<D>(row, 2 * e2 + 1) + 8 * h);
-      u32x4 raw;
-      raw[0] = x0[0]; raw[1] = x0[1]; raw[2] = x1[0]; raw[3] = x1[1];
-      o[ds] = mfma32(__builtin_bit_cast(bf16x8, raw), b, o[ds]);
-    }
-  }
-}
-
-// Key offset (within a 32-key score block) of result register v for lane half h.
-__device__ __forceinline__ int key_of(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
-
-// The running max is only raised when a row's new scores exceed it by more than kSlack (log2
-// units); otherwise probabilities up to 2^kSlack are accumulated against the old max.  With
-// N <= 2^22 keys, sums stay below 2^54 times the largest |v|, far inside fp32 range, and bf16
-// probabilities keep their relative precision.  Rescaling the accumulators is then rare, and is
-// skipped by the whole wave when no lane needs it.
-constexpr float kSlack = 32.0f;
-
-// One 64-key stage (K and V tiles in LDS) folded into this lane's running softmax.
-// active: this row takes part; nvalid: keys of the stage below N.
-template <int D>
-__device__ __forceinline__ void exact_stage(const lds_u8* ktile, const lds_u8* vtile,
-                                            const bf16x8 (&qf)[D / 16], bool active, int nvalid,
-                                            float sl2, float& mrun, float& lsum,
-                                            f32x16 (&o)[D / 32]) {
-  constexpr int NS = kStage / 32;
-  const int h = (threadIdx.x & 63) >> 5;
-  f32x16 s[NS];
-#pragma unroll
-  for (int kb = 0; kb < NS; ++kb) s[kb] = scores32<D>(ktile, 32 * kb, qf, f32x16{});
-
-  const bool partial = nvalid < kStage;  // wave-uniform
-  if (partial) {
-#pragma unroll
-    for (int kb = 0; kb < NS; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        if (32 * kb + key_of(v, h) >= nvalid) s[kb][v] = -INFINITY;
-  }
-  float mt = -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < NS; ++kb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[kb][v]);
-  mt = pair_max(mt) * sl2;
-  const bool grow = active && mt > mrun + kSlack;
-  if (__builtin_amdgcn_ballot_w64(grow)) {
-    const float mnew = grow ? mt : mrun;
-    const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
-    mrun = mnew;
-    lsum *= alpha;
-#pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[ds][v] *= alpha;
-  }
-  // rows that do not take part subtract +inf: every probability is 0
-  const float moff = active ? -mrun : -INFINITY;
-  uint32_t pk[NS][8];
-  float ps = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < NS; ++kb) {
-    float p[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(fmaf(s[kb][v], sl2, moff));
-    ps = round_p(p, pk[kb], ps);
-  }
-  lsum += ps;
-#pragma unroll
-  for (int kb = 0; kb < NS; ++kb) pv32<D>(vtile, 32 * kb, pk[kb], o);
-}
-
-// ---------------------------------------------------------------------------------------------
-// Software-pipelined exact loop, in steps of 32 keys (half a 64-key stage).  A wave keeps two
-// score blocks live: while the matrix cores compute S^T of the next 32 keys (phase A), the vector
-// ALU turns the current 32 keys' scores into probabilities; while the matrix cores accumulate
-// O^T += V^T P^T for the current 32 keys (phase B), the vector ALU takes the next block's row
-// maximum.  K and V tiles are double buffered separately, each with its own barrier, so the next
-// stage's keys can be in use while this stage's values still are.  Instruction groups are
-// interleaved with sched_group_barrier so that every MFMA has independent vector work behind it.
-// ---------------------------------------------------------------------------------------------
-constexpr int kSgMfma = 0x008, kSgValu = 0x002 | 0x400, kSgDsRead = 0x100;
-
-// Phase A: (QK) sn = S^T of the 32 keys at rows kr0.. of ktile, and the probabilities of the
-// current block sc (offset moff = -running max, or -inf for rows that do not take part) packed
-// into pk, with their rounded sum added to ps.
-template <int D, bool QK>
-__device__ __forceinline__ void phase_a(const lds_u8* ktile, int kr0, const bf16x8 (&qf)[D / 16],
-                                        f32x16& sn, const f32x16& sc, float sl2, float moff,
-                                        uint32_t (&pk)[8], float& ps) {
-  constexpr int NM = D / 16;        // MFMAs
-  constexpr int PER = 16 / NM;      // probabilities per MFMA slot (even)
-  const int lane = threadIdx.x & 63;
-  const int c = lane & 31, h = lane >> 5;
-  if constexpr (QK) sn = f32x16{};
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    if constexpr (QK) {
-      const u32x4 raw = lds_read16(ktile + tile_off<D>(kr0 + c, 2 * i + h));
-      sn = mfma32(__builtin_bit_cast(bf16x8, raw), qf[i], sn);
-    }
-#pragma unroll
-    for (int u = 0; u < PER; u += 2) {
-      const int v = i * PER + u;
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[v], sl2, moff));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[v + 1], sl2, moff));
-      pk[v / 2] = pack_bf16x2(p0, p1);
-      ps = add_bf16x2(pk[v / 2], ps);
-    }
-  }
-  if constexpr (QK) {
-    // K operand reads run three MFMAs ahead
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 3, 0);
-#pragma unroll
-    for (int i = 0; i < NM; ++i) {
-      if (i + 3 < NM) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgValu, 3 * PER, 0);
-    }
-  }
-}
-
-// Phase B: O^T += V^T P^T for the 32 keys at rows vr0.. of vtile and, when MX, the maximum of the
-// next block's scores sn (raw, before scaling).
-template <int D, bool MX>
-__device__ __forceinline__ float phase_b(const lds_u8* vtile, int vr0, const uint32_t (&pk)[8],
-                                         const f32x16& sn, f32x16 (&o)[D / 32]) {
-  constexpr int NM = 2 * (D / 32);  // MFMAs
-  constexpr int PER = 16 / NM;      // maxima per MFMA slot
-  const int lane = threadIdx.x & 63;
-  const int grp = lane >> 4, j = lane & 15;
-  const int h = grp >> 1, cg = grp & 1;
-  float m0 = -INFINITY, m1 = -INFINITY;
-#pragma unroll
-  for (int e2 = 0; e2 < 2; ++e2) {
-    const bf16x8 b = p_operand(pk, e2);
-#pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds) {
-      const int d0 = 32 * ds + 16 * cg + 4 * (j & 3);
-      s16x4 x[2];
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int row = vr0 + 16 * e2 + 8 * r + 4 * h + (j >> 2);
-        const lds_u8* p = vtile + tile_off<D>(row, d0 >> 3) + ((d0 >> 2) & 1) * 8;
-        x[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(p));
-      }
-      u32x4 raw;
-      raw[0] = __builtin_bit_cast(u32x2, x[0])[0];
-      raw[1] = __builtin_bit_cast(u32x2, x[0])[1];
-      raw[2] = __builtin_bit_cast(u32x2, x[1])[0];
-      raw[3] = __builtin_bit_cast(u32x2, x[1])[1];
-      o[ds] = mfma32(__builtin_bit_cast(bf16x8, raw), b, o[ds]);
-      if constexpr (MX) {
-        const int step = e2 * (D / 32) + ds;
-#pragma unroll
-        for (int u = 0; u < PER; u += 2) {
-          m0 = fmaxf(m0, sn[step * PER + u]);
-          m1 = fmaxf(m1, sn[step * PER + u + 1]);
-        }
-      }
-    }
-  }
-  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    if (i + 2 < NM) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-    if constexpr (MX) __builtin_amdgcn_sched_group_barrier(kSgValu, PER, 0);
-  }
-  return fmaxf(m0, m1);
-}
-
-// Keys of a 32-key block at or beyond nvalid (counted from the block's first key) get -inf.
-__device__ __forceinline__ void mask_tail(f32x16& s, int nvalid) {
-  const int h = (threadIdx.x & 63) >> 5;
-#pragma unroll
-  for (int v = 0; v < 16; ++v)
-    if (key_of(v, h) >= nvalid) s[v] = -INFINITY;
-}
-
-// Raise the running max to the block maximum mt_raw (raw score units) when it exceeds it by more
-// than kSlack, rescaling the accumulators; rows that do not take part never raise it.
-template <int D>
-__device__ __forceinline__ void raise_max(float mt_raw, bool active, float sl2, float& mrun,
-                                          float& lsum, f32x16 (&o)[D / 32]) {
-  const float mt = pair_max(mt_raw) * sl2;
-  const bool grow = active && mt > mrun + kSlack;
-  if (__builtin_amdgcn_ballot_w64(grow)) {
-    const float mnew = grow ? mt : mrun;
-    const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
-    mrun = mnew;
-    lsum *= alpha;
-#pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[ds][v] *= alpha;
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void load_q(const uint16_t* __restrict__ qrow, bool valid,
-                                       bf16x8 (&qf)[D / 16]) {
-  const int h = (threadIdx.x & 63) >> 5;
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (valid) raw = *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * h);
-    qf[kk] = __builtin_bit_cast(bf16x8, raw);
-  }
-}
-
-// Write O = O^T / l for the wave's 32 rows: through LDS (row-major, swizzled) so that each global
-// store instruction writes whole rows.  stage: this wave's 32 x D bf16 LDS area.  Also the
-// optional fp32 output and log-sum-exp.  Called by every lane of the wave.
-template <int D>
-__device__ __forceinline__ void epilogue(const f32x16 (&o)[D / 32], float mrun, float lsum,
-                                         int64_t row0, int64_t N, uint16_t* __restrict__ out,
-                                         int64_t on, float* __restrict__ out_f32,
-                                         float* __restrict__ lse, lds_u8* stage) {
-  const int lane = threadIdx.x & 63;
-  const int c = lane & 31, h = lane >> 5;
-  const int64_t row = row0 + c;
-  const float l = pair_sum(lsum);
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
-#pragma unroll
-  for (int ds = 0; ds < D / 32; ++ds)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float x0 = o[ds][4 * g + 0] * inv, x1 = o[ds][4 * g + 1] * inv;
-      const float x2 = o[ds][4 * g + 2] * inv, x3 = o[ds][4 * g + 3] * inv;
-      u32x2 w;
-      w[0] = pack_bf16x2(x0, x1);
-      w[1] = pack_bf16x2(x2, x3);
-      // d = 32 ds + 8 g + 4 h + (0..3): chunk 4 ds + g, half h
-      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
-          stage + tile_off<D>(c, 4 * ds + g) + 8 * h) = w;
-      if (out_f32 && row < N)
-        *reinterpret_cast<f32x4*>(out_f32 + row * D + 32 * ds + 8 * g + 4 * h) = f32x4{x0, x1, x2, x3};
-    }
-  if (lse && h == 0 && row < N) lse[row] = l > 0.f ? (mrun + log2f(l)) * kLn2 : -INFINITY;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  constexpr int kChunks = D / 8;
-#pragma unroll
-  for (int i = 0; i < 32 * kChunks / 64; ++i) {
-    const int idx = i * 64 + lane;
-    const int r = idx / kChunks, ch = idx % kChunks;
-    const u32x4 v = lds_read16(stage + tile_off<D>(r, ch));
-    if (row0 + r < N) *reinterpret_cast<u32x4*>(out + (row0 + r) * on + ch * 8) = v;
-  }
-}
-
-// Work item of this workgroup, XCD-aware: workgroup i runs on XCD i % 8, so XCD x is given the
-// contiguous range of (head, query tile) items x*P .. x*P + P - 1 and the tiles of one head that
-// run at the same time share that XCD's L2.  Returns false for the padding workgroups.
-__device__ __forceinline__ bool work_item(int64_t total, int64_t& w) {
-  const int64_t per = (total + 7) / 8;
-  w = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
-  return w < total;
-}
-
-}  // namespace
-
-// ---------------------------------------------------------------------------------------------
-// Row statistics: mu, sigma, tau of every query's proxy row
-// ---------------------------------------------------------------------------------------------
-
-template <int D>
-__global__ __launch_bounds__(kRowStatsThreads) void rowstats_kernel(RowStatsArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  lds_u8* smem = (lds_u8*)smem_raw;
-  constexpr int64_t kGroupRows = (int64_t)kRowStatsRows * kRowStatsPasses;
-  const int64_t groups = (a.N + kGroupRows - 1) / kGroupRows;
-  const int64_t bh = blockIdx.x / groups;
-  const int64_t grp = blockIdx.x % groups;
-  const int lane = threadIdx.x & 63, c = lane & 31, h = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-
-  // C pieces (dominant directions removed) -> LDS, smallest first: tile p holds piece lo (p = 0),
-  // mid (1), hi (2); then the mean pooled key and the dominant directions, both fp64
-  const uint16_t* cbase = a.cp + bh * D * D;
-  const int64_t piece = a.BH * D * D;
-#pragma unroll
-  for (int p = 0; p < 3; ++p)
-    load_tile<D, D, kRowStatsThreads>(cbase + (2 - p) * piece, 0, D, smem + p * D * D * 2);
-  double* kgl = (double*)(smem_raw + 3 * D * D * 2);
-  double* ftl = kgl + D;  // [kFactorTop][D]
-  const int ntop = __builtin_amdgcn_readfirstlane(a.ftop[bh]);
-  for (int i = threadIdx.x; i < D; i += kRowStatsThreads) kgl[i] = a.kglob[bh * D + i];
-  for (int i = threadIdx.x; i < kFactorTop * D; i += kRowStatsThreads)
-    ftl[i] = i < ntop * D ? a.f64top[bh * kFactorTop * D + i] : 0.0;
-  wait_vmcnt<0>();
-  __syncthreads();
-
-  // C operand of (piece p, k step kk, row tile ab): row 32 ab + c, chunk 2 kk + h.  The row swizzle
-  // reads row bits below 5 only, so ab and p add whole tiles and kk flips chunk bits:
-  // offset = p D D 2 + ab 32 2D + (crel ^ (kk << 5)).
-  const int crel = c * (2 * D) + (swz<D>(c, h) << 4);
-  const uint16_t* qhead = a.q + a.qs.base(bh);
-  for (int pp = 0; pp < kRowStatsPasses; ++pp) {
-    const int64_t r0 = grp * kGroupRows + (int64_t)pp * kRowStatsRows;
-    if (r0 >= a.N) break;
-    const int64_t row0w = r0 + wave * 32;  // this wave's first row
-    const int64_t row = row0w + c;
-    const bool valid = row < a.N;
-    // the wave's rows through a buffer resource that ends after its last valid row: rows past N
-    // read as zeros without a branch per load
-    const int64_t nrows = a.N - row0w < 32 ? a.N - row0w : 32;
-    const uint32_t bytes = nrows > 0 ? (uint32_t)((nrows - 1) * a.qs.sn * 2 + D * 2) : 0u;
-    const __amdgpu_buffer_rsrc_t qrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(qhead + row0w * a.qs.sn), (short)0, (int)bytes,
-                                          0x00020000);
-    const uint32_t qoff = (uint32_t)(c * a.qs.sn * 2);
-    // B operand of k step kk, lane half h: q at d = 16 kk + 4 h + 0..3 and 16 kk + 8 + 4 h + 0..3 (the
-    // pieces of C store their columns in the same order, see the pooled-key statistics).  These are
-    // exactly the rows of C q this lane half receives, so the same registers serve q^T (C q):
-    // element e of qf[kk] is q at d = 16 kk + 8 (e / 4) + 4 h + e % 4.
-    bf16x8 qf[D / 16];
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const u32x2 lo = __builtin_bit_cast(
-          u32x2, __builtin_amdgcn_raw_buffer_load_b64(qrs, qoff + (16 * kk + 4 * h) * 2, 0, 0));
-      const u32x2 hi = __builtin_bit_cast(
-          u32x2, __builtin_amdgcn_raw_buffer_load_b64(qrs, qoff + (16 * kk + 8 + 4 * h) * 2, 0, 0));
-      qf[kk] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-    }
-    // all of the pass's loads are issued here, ahead of the matrix work that hides their latency
-    __builtin_amdgcn_sched_barrier(0);
-    // y[ab][v] = (C q)[32 ab + 8 (v/4) + 4 h + v%4]: D/32 independent accumulation chains,
-    // pieces smallest first; the operand reads of step s + 1 are issued before step s's matrix
-    // instructions
-    constexpr int S = 3 * (D / 16);
-    f32x16 y[D / 32];
-#pragma unroll
-    for (int ab = 0; ab < D / 32; ++ab) y[ab] = f32x16{};
-    u32x4 ra[2][D / 32];
-    auto read_step = [&](int s, u32x4 (&dst)[D / 32]) {
-      const lds_u8* base = smem + (s / (D / 16)) * D * D * 2 + (crel ^ ((s % (D / 16)) << 5));
-#pragma unroll
-      for (int ab = 0; ab < D / 32; ++ab) dst[ab] = lds_read16(base + ab * 32 * 2 * D);
-    };
-    read_step(0, ra[0]);
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      if (s + 1 < S) read_step(s + 1, ra[(s + 1) & 1]);
-#pragma unroll
-      for (int ab = 0; ab < D / 32; ++ab)
-        y[ab] = mfma32(__builtin_bit_cast(bf16x8, ra[s & 1][ab]), qf[s % (D / 16)], y[ab]);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, D / 32, 0);
-#pragma unroll
-    for (int s = 0; s + 1 < S; ++s) {
-      __builtin_amdgcn_sched_group_barrier(kSgDsRead, D / 32, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, D / 32, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, D / 32, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    // q^T (C q) over this lane half's rows: y[ab][v] is row 32 ab + 8 g + 4 h + i (g = v / 4,
-    // i = v % 4), whose query element is element 4 (g % 2) + i of qf[2 ab + g / 2]
-    float vpart = 0.f;
-#pragma unroll
-    for (int ab = 0; ab < D / 32; ++ab)
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        vpart = fmaf(y[ab][v], (float)qf[2 * ab + (v >> 3)][v & 7], vpart);
-    // q . g over this lane half's D/2 elements, in fp64 (products and sums of the bf16 query
-    // with the fp64 mean pooled key), and for heads with dominant directions (none for most) also
-    // w_k . q in fp64, their squares summed into vtop.  Each query element is
-    // converted where it is used, and the LDS offset is opaque to the optimiser, so that neither
-    // the converted query nor the fp64 operands are held in registers across the pass loop.
-    int hofs = 4 * h;
-    __asm__ __volatile__("" : "+v"(hofs));
-    double mpart = 0.0, vtop = 0.0;
-    if (ntop == 0) {
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          mpart = fma((double)(float)qf[kk][e], kgl[16 * kk + 8 * (e >> 2) + hofs + (e & 3)], mpart);
-    } else {
-      double z[kFactorTop] = {};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const double qd = (double)(float)qf[kk][e];
-          const int idx = 16 * kk + 8 * (e >> 2) + hofs + (e & 3);
-          mpart = fma(qd, kgl[idx], mpart);
-#pragma unroll
-          for (int kt = 0; kt < kFactorTop; ++kt) z[kt] = fma(qd, ftl[kt * D + idx], z[kt]);
-        }
-#pragma unroll
-      for (int kt = 0; kt < kFactorTop; ++kt) {  // rows past ntop are zero in LDS
-        const double zz = z[kt] + __shfl_xor(z[kt], 32);
-        vtop = fma(zz, zz, vtop);
-      }
-    }
-    const double mu64 = (mpart + __shfl_xor(mpart, 32)) / sqrt((double)D);
-    const float mu = (float)mu64;
-    const float var = (float)((vtop + (double)pair_sum(vpart)) / (double)D);
-    const float sigma = sqrtf(fmaxf(var, 0.f));
-    const float tau = isinf(a.beta) ? a.beta : (float)fma((double)a.beta, (double)sigma, mu64);
-    // sigma = 0 (one key block, q = 0, or identical pooled keys): every proxy of the row equals
-    // mu = tau, so s >= tau keeps every block and the row is dense.  The fused kernel's s and this
-    // mu are rounded along different paths and need not compare equal, so the threshold it reads
-    // says so directly; the exported tau stays mu + beta * sigma.
-    const float tau_sel = (!isinf(a.beta) && var <= 0.f) ? -INFINITY : tau;
-    if (valid && h == 0) {
-      a.tau[bh * a.N + row] = tau_sel;
-      if (a.mu) a.mu[bh * a.N + row] = mu;
-      if (a.sigma) a.sigma[bh * a.N + row] = sigma;
-      if (a.tau_out) a.tau_out[bh * a.N + row] = tau;
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------------------------
 // Fused Sol-Attn kernel
@@ -1673,214 +913,6 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
                 smem + wave * 16 * D * 2);
 }
 
-// Half HB of stage n of the pipelined exact loop over consecutive stages (dense kernel); B = n & 1.
-// NEXT: a next 32-key block exists (it may be partial).  sc holds the current block's scores,
-// sn receives the next block's.  K tiles live at kbuf + b * tile, V tiles at vbuf + b * tile.
-// Copies are issued K0, V0, K1 (prologue), then V_{n+1} at half 0 and K_{n+2} at half 1 of stage n.
-template <int D, int B, int HB, bool NEXT, int NT>
-__device__ __forceinline__ void dense_half(int n, int nst, int64_t N, const uint16_t* kb,
-                                           const uint16_t* vb, int64_t rs, lds_u8* kbuf,
-                                           lds_u8* vbuf, const TileOffsets<D, kStage, NT>& toff,
-                                           const bf16x8 (&qf)[D / 16], float sl2,
-                                           const f32x16& sc, f32x16& sn, float& mrun,
-                                           float& lsum, f32x16 (&o)[D / 32]) {
-  constexpr int kTileBytes = kStage * D * 2;
-  constexpr int L = tile_loads<D, kStage, NT>();
-  auto issue = [&](const uint16_t* src, int st, lds_u8* dst) {
-    load_rows<D, kStage, NT>(src, (int64_t)st * kStage, N, rs, toff, dst);
-  };
-  const bool more = n + 1 < nst;
-  if constexpr (HB == 0) {
-    // V_n has landed (only K_{n+1}, issued after it, may be in flight); after the barrier every
-    // wave is done with V_{n-1}, whose buffer takes V_{n+1}
-    if (more) wait_vmcnt<L>();
-    else wait_vmcnt<0>();
-    bar();
-    if (more) issue(vb, n + 1, vbuf + (B ^ 1) * kTileBytes);
-  } else {
-    // K_{n+1} has landed (only V_{n+1} may be in flight); after the barrier every wave is done
-    // with K_n, whose buffer takes K_{n+2}
-    if (more) wait_vmcnt<L>();
-    bar();
-    if (n + 2 < nst) issue(kb, n + 2, kbuf + B * kTileBytes);
-  }
-  uint32_t pk[8];
-  float ps = 0.f;
-  const lds_u8* knext = HB == 0 ? kbuf + B * kTileBytes : kbuf + (B ^ 1) * kTileBytes;
-  phase_a<D, NEXT>(knext, HB == 0 ? 32 : 0, qf, sn, sc, sl2, -mrun, pk, ps);
-  if constexpr (NEXT) {
-    const int nv = (int)(N - (int64_t)n * kStage) - (HB == 0 ? 32 : 64);
-    if (nv < 32) mask_tail(sn, nv);
-  }
-  lsum += ps;
-  if constexpr (NEXT) {
-    const float mt = phase_b<D, true>(vbuf + B * kTileBytes, 32 * HB, pk, sn, o);
-    raise_max<D>(mt, true, sl2, mrun, lsum, o);
-  } else {
-    phase_b<D, false>(vbuf + B * kTileBytes, 32 * HB, pk, sn, o);
-  }
-}
-
-// ---------------------------------------------------------------------------------------------
-// Full proxy map (the prior-art routing's input): s_map[bh][i][j] = q_i . Kbar_j / sqrt(d) for
-// every row and block, written to memory -- the round trip the fused kernel avoids.  The same
-// fp32-accurate three-piece product as the fused kernel's routing sweep, one workgroup per
-// 128-row tile, pooled-key chunks double buffered.  Row-major: a wave's 32 x 32 chunk of scores is
-// transposed through LDS so that every store writes whole 128-byte row segments.
-// ---------------------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void proxy_map_kernel(const uint16_t* __restrict__ q,
-                                                                Strides qs,
-                                                                const uint16_t* __restrict__ kp,
-                                                                int64_t BH, int64_t N, int64_t M,
-                                                                int64_t Mp, float* __restrict__ smap) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  lds_u8* smem = (lds_u8*)smem_raw;
-  constexpr int kChunkTile = 32 * D * 2;
-  constexpr int kBuf = 3 * kChunkTile;
-  constexpr int kStageStride = 33;  // floats per staged row (33: conflict-free column writes)
-  const int t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63, c = lane & 31, h = lane >> 5;
-  const int64_t ntiles = (N + kQTile - 1) / kQTile;
-  int64_t w;
-  if (!work_item(BH * ntiles, w)) return;
-  const int64_t bh = w / ntiles;
-  const int64_t tile = w % ntiles;
-  const int64_t row = tile * kQTile + wave * 32 + c;
-  const bool rvalid = row < N;
-  bf16x8 qf[D / 16];
-  load_q<D>(q + qs.base(bh) + row * qs.sn, rvalid, qf);
-  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
-  const int64_t piece = BH * Mp * D;
-  const uint16_t* kp0 = kp + bh * Mp * D;
-  const int64_t row0 = tile * kQTile + wave * 32;
-  float* stage = (float*)(smem_raw + 2 * kBuf) + wave * 32 * kStageStride;  // this wave's 32 x 32
-  const int nchunks = (int)(Mp / 32);
-  const TileOffsets<D, 32> coff(D);
-  auto issue_chunk = [&](int cb, int b) {
-    lds_u8* base = smem + b * kBuf;
-    load_dense_rows<D, 32>(kp0 + 2 * piece, (int64_t)cb * 32, coff, base);
-    load_dense_rows<D, 32>(kp0 + 1 * piece, (int64_t)cb * 32, coff, base + kChunkTile);
-    load_dense_rows<D, 32>(kp0, (int64_t)cb * 32, coff, base + 2 * kChunkTile);
-  };
-  issue_chunk(0, 0);
-  for (int cb = 0; cb < nchunks; ++cb) {
-    const int b = cb & 1;
-    wait_vmcnt<0>();
-    bar();
-    if (cb + 1 < nchunks) issue_chunk(cb + 1, b ^ 1);
-    const lds_u8* base = smem + b * kBuf;
-    f32x16 acc = {};
-#pragma unroll
-    for (int p = 0; p < 3; ++p) acc = scores32<D>(base + p * kChunkTile, 0, qf, acc);
-    // stage[r][kj] = score of row r, block kj of the chunk; then each store instruction writes
-    // two rows' 32 consecutive scores (lane l: block l % 32 of rows l / 32 + 2 i)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) stage[c * kStageStride + key_of(v, h)] = acc[v] * inv_sqrt_d;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int64_t j = (int64_t)cb * 32 + c;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = h + 2 * i;
-      const int64_t grow = row0 + r;
-      if (grow < N && j < M) smap[(bh * N + grow) * M + j] = stage[r * kStageStride + c];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
-}
-
-// ---------------------------------------------------------------------------------------------
-// Dense reference kernel: the exact loop over every key, no routing.
-// ---------------------------------------------------------------------------------------------
-
-// WAVES waves of 32 rows per workgroup: 4 (two workgroups per CU) or 8 (one workgroup per CU,
-// every K/V stage copied into LDS feeding 256 rows).
-template <int D, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void dense_attn_kernel(const uint16_t* __restrict__ q,
-                                                                 const uint16_t* __restrict__ k,
-                                                                 const uint16_t* __restrict__ v,
-                                                                 Strides in,
-                                                                 uint16_t* __restrict__ out,
-                                                                 Strides outs,
-                                                                 float* __restrict__ lse,
-                                                                 int64_t BH, int64_t N) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  lds_u8* smem = (lds_u8*)smem_raw;
-  constexpr int kTileBytes = kStage * D * 2;
-  constexpr int NT = 64 * WAVES;
-  constexpr int QT = 32 * WAVES;
-  const int t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63, c = lane & 31;
-  const int64_t ntiles = (N + QT - 1) / QT;
-  int64_t w;
-  if (!work_item(BH * ntiles, w)) return;
-  const int64_t bh = w / ntiles;
-  const int64_t tile = w % ntiles;
-  const int64_t row0 = tile * QT + wave * 32;
-  const int64_t row = row0 + c;
-  const bool rvalid = row < N;
-  const uint16_t* kb = k + in.base(bh);
-  const uint16_t* vb = v + in.base(bh);
-  const int64_t sn = in.sn;
-
-  bf16x8 qf[D / 16];
-  load_q<D>(q + in.base(bh) + row * sn, rvalid, qf);
-  const float sl2 = kLog2e / sqrtf((float)D);
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int ds = 0; ds < D / 32; ++ds) o[ds] = f32x16{};
-  float mrun = -1e30f, lsum = 0.f;
-
-  const int nst = (int)((N + kStage - 1) / kStage);
-  const TileOffsets<D, kStage, NT> toff(sn);
-  lds_u8* kbuf = smem;                        // K tiles: kbuf + b * kTileBytes
-  lds_u8* vbuf = smem + 2 * kTileBytes;       // V tiles
-  auto issue = [&](const uint16_t* src, int st, lds_u8* dst) {
-    load_rows<D, kStage, NT>(src, (int64_t)st * kStage, N, sn, toff, dst);
-  };
-
-  // prologue: K0, V0, K1 in LDS; scores and max of the first 32 keys
-  issue(kb, 0, kbuf);
-  issue(vb, 0, vbuf);
-  if (nst > 1) issue(kb, 1, kbuf + kTileBytes);
-  wait_vmcnt<0>();
-  bar();
-  f32x16 sa = scores32<D>(kbuf, 0, qf, f32x16{}), sb;
-  if (N < 32) mask_tail(sa, (int)N);
-  {
-    float m = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) m = fmaxf(m, sa[v]);
-    mrun = pair_max(m) * sl2;
-  }
-  // stages n (buffers 0) and n + 1 (buffers 1) per iteration; the last stage's half 1 has no
-  // next block
-  int n = 0;
-  for (; n + 2 < nst; n += 2) {
-    dense_half<D, 0, 0, true, NT>(n, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
-    dense_half<D, 0, 1, true, NT>(n, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
-    dense_half<D, 1, 0, true, NT>(n + 1, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
-    dense_half<D, 1, 1, true, NT>(n + 1, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
-  }
-  if (n + 1 < nst) {
-    dense_half<D, 0, 0, true, NT>(n, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
-    dense_half<D, 0, 1, true, NT>(n, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
-    dense_half<D, 1, 0, true, NT>(n + 1, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
-    dense_half<D, 1, 1, false, NT>(n + 1, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
-  } else {
-    dense_half<D, 0, 0, true, NT>(n, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sa, sb, mrun, lsum, o);
-    dense_half<D, 0, 1, false, NT>(n, nst, N, kb, vb, sn, kbuf, vbuf, toff, qf, sl2, sb, sa, mrun, lsum, o);
-  }
-  bar();  // stage buffers free for the epilogue
-  epilogue<D>(o, mrun, lsum, row0, N, out + outs.base(bh), outs.sn, nullptr,
-              lse ? lse + bh * N : nullptr,
-              smem + wave * 32 * D * 2);
-}
-
 // ---------------------------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------------------------
@@ -1891,14 +923,6 @@ static size_t sparse_smem_bytes(int d, int64_t Mp, int halves) {
   const size_t regionA = 2 * stage > 2 * route ? 2 * stage : 2 * route;
   return regionA + (size_t)halves * (Mp / 32) * 4;
 }
-
-template <typename K>
-static hipError_t set_smem(K kern, size_t bytes) {
-  return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)bytes);
-}
-
-static unsigned xcd_grid(int64_t total) { return (unsigned)(((total + 7) / 8) * 8); }
 
 template <int D, int BLK, int WAVES>
 static hipError_t launch_sparse_t(const SparseArgs& a, hipStream_t stream) {
@@ -1930,69 +954,6 @@ hipError_t launch_sparse(int d, const SparseArgs& a, hipStream_t stream) {
   if (d == 64 && a.block == 128) return launch_sparse_t<64, 128, 4>(a, stream);
   if (d == 128 && a.block == 64) return launch_sparse16_t<128, 64>(a, stream);
   return launch_sparse16_t<128, 128>(a, stream);
-}
-
-template <int D>
-static hipError_t launch_rowstats_t(const RowStatsArgs& a, hipStream_t stream) {
-  const size_t smem = (size_t)3 * D * D * 2 + (size_t)(1 + kFactorTop) * D * sizeof(double);
-  auto kern = rowstats_kernel<D>;
-  hipError_t err = set_smem(kern, smem);
-  if (err != hipSuccess) return err;
-  constexpr int64_t kGroupRows = (int64_t)kRowStatsRows * kRowStatsPasses;
-  const int64_t groups = (a.N + kGroupRows - 1) / kGroupRows;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(a.BH * groups)), dim3(kRowStatsThreads), smem, stream, a);
-  return hipGetLastError();
-}
-
-template <int D>
-static hipError_t launch_proxy_map_t(const uint16_t* q, const Strides& qs, const uint16_t* kp,
-                                     int64_t BH, int64_t N, int64_t M, int64_t Mp, float* s_map,
-                                     hipStream_t stream) {
-  const size_t smem = (size_t)2 * 3 * 32 * D * 2 + (size_t)4 * 32 * 33 * sizeof(float);
-  auto kern = proxy_map_kernel<D>;
-  hipError_t err = set_smem(kern, smem);
-  if (err != hipSuccess) return err;
-  const int64_t ntiles = (N + kQTile - 1) / kQTile;
-  hipLaunchKernelGGL(kern, dim3(xcd_grid(BH * ntiles)), dim3(kThreads), smem, stream, q, qs, kp, BH,
-                     N, M, Mp, s_map);
-  return hipGetLastError();
-}
-
-hipError_t launch_proxy_map(int d, const uint16_t* q, const Strides& qs, const uint16_t* kp,
-                            int64_t BH, int64_t N, int64_t M, int64_t Mp, float* s_map,
-                            hipStream_t stream) {
-  return d == 64 ? launch_proxy_map_t<64>(q, qs, kp, BH, N, M, Mp, s_map, stream)
-                 : launch_proxy_map_t<128>(q, qs, kp, BH, N, M, Mp, s_map, stream);
-}
-
-hipError_t launch_rowstats(int d, const RowStatsArgs& a, hipStream_t stream) {
-  return d == 64 ? launch_rowstats_t<64>(a, stream) : launch_rowstats_t<128>(a, stream);
-}
-
-// Eight waves (256 rows, one workgroup per CU) at d = 128: each K/V stage feeds twice the rows,
-// 2% faster at the Wan2.1-14B shape (109 vs 111 ms, interleaved); four waves (two workgroups per
-// CU) at d = 64, where eight were 10% slower on LTX's smaller grid.
-template <int D>
-static hipError_t launch_dense_t(int64_t BH, int64_t N, const void* q, const void* k,
-                                 const void* v, const Strides& in, void* out, const Strides& outs,
-                                 float* lse, hipStream_t stream) {
-  constexpr int kDenseWaves = D == 128 ? 8 : 4;
-  const size_t smem = (size_t)4 * kStage * D * 2;
-  auto kern = dense_attn_kernel<D, kDenseWaves>;
-  hipError_t err = set_smem(kern, smem);
-  if (err != hipSuccess) return err;
-  const int64_t ntiles = (N + 32 * kDenseWaves - 1) / (32 * kDenseWaves);
-  hipLaunchKernelGGL(kern, dim3(xcd_grid(BH * ntiles)), dim3(64 * kDenseWaves), smem, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, in,
-                     (uint16_t*)out, outs, lse, BH, N);
-  return hipGetLastError();
-}
-
-hipError_t launch_dense(int d, int64_t BH, int64_t N, const void* q, const void* k, const void* v,
-                        const Strides& in, void* out, const Strides& outs, float* lse,
-                        hipStream_t stream) {
-  return d == 64 ? launch_dense_t<64>(BH, N, q, k, v, in, out, outs, lse, stream)
-                 : launch_dense_t<128>(BH, N, q, k, v, in, out, outs, lse, stream);
 }
 
 }  // namespace solattn
