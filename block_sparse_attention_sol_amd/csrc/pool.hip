@@ -41,7 +41,9 @@ __device__ __forceinline__ float chunk_sum(float x) {
 // wave takes kPoolPerWave of them.  A wave loads whole rows (lane l: 16-byte chunk l % C of rows
 // l / C, l / C + 64 / C, ...), keeps fp32 sums of its chunk, and combines the lanes that share a
 // chunk with cross-lane operations (fixed order: deterministic).  The mean divides by n_j.  Vbar^T
-// is staged in LDS and written as one 2 x kPoolBlocks-byte run per head-dimension row.
+// is staged in LDS and written as one 2 x kPoolBlocks-byte run per head-dimension row.  K and V
+// are streamed with non-temporal loads (each byte is read once; the attention kernel that follows
+// reads the heads again from the first, long after these lines would have left the caches).
 template <int D>
 __global__ __launch_bounds__(64 * kPoolWaves) void pool_kv_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, Strides kv, int64_t N, int block,
@@ -75,9 +77,9 @@ __global__ __launch_bounds__(64 * kPoolWaves) void pool_kv_kernel(
         for (int u = 0; u < U; ++u) {
           const int64_t r = r0 + u * RS + rs;
           a[u] = b[u] = u32x4{0u, 0u, 0u, 0u};
-          if (r < hi) {
-            a[u] = *reinterpret_cast<const u32x4*>(kb + r * kv.sn + cc * 8);
-            b[u] = *reinterpret_cast<const u32x4*>(vb + r * kv.sn + cc * 8);
+          if (r < hi) {  // read once here: non-temporal loads
+            a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + r * kv.sn + cc * 8));
+            b[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + r * kv.sn + cc * 8));
           }
         }
 #pragma unroll
