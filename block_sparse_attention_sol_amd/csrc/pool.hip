@@ -4,10 +4,10 @@
 // score of the Sol-Attn page's routing paragraph is q . Kbar_j / sqrt(d), and Vbar_j is the value
 // of block j's pooled token.
 //
-// One workgroup pools 32 consecutive key blocks of one (batch, head) for both K and V: each wave
-// reads its blocks' rows as 16-byte chunks (consecutive lanes -> consecutive chunks of a row, so
-// each load instruction covers whole rows), accumulates fp32 sums and combines the lanes sharing a
-// chunk with cross-lane operations in a fixed order (deterministic).  Besides the fp32 means it
+// One workgroup pools 32 (small heads: 8) consecutive key blocks of one (batch, head) for both K
+// and V: each wave reads its blocks' rows as 16-byte chunks (consecutive lanes -> consecutive
+// chunks of a row, so each load instruction covers whole rows), accumulates fp32 sums and combines
+// the lanes sharing a chunk with cross-lane operations in a fixed order (deterministic).  Besides the fp32 means it
 // writes the layouts the attention kernel consumes:
 //   kp   [3][BH][Mp][d] bf16: Kbar split into hi + mid + lo bf16 pieces whose sum is the fp32
 //        value, so a bf16 matrix product over the three pieces reproduces fp32 proxies;
@@ -23,8 +23,11 @@
 namespace solattn {
 
 constexpr int kPoolWaves = 8;                // waves per pooling workgroup
-constexpr int kPoolBlocks = 32;              // key blocks per pooling workgroup
-constexpr int kPoolPerWave = kPoolBlocks / kPoolWaves;
+// key blocks per pooling workgroup: 32, or 8 (one per wave) when 32 would give fewer than
+// kPoolMinGroups workgroups (small heads: more workgroups in flight, one round trip per wave)
+constexpr int kPoolBlocks = 32;
+constexpr int kPoolBlocksSmall = 8;
+constexpr int64_t kPoolMinGroups = 512;
 
 // Sum of x over the lanes that hold the same 16-byte chunk of a row: lanes l, l + C, l + 2C, ...
 // for C = D / 8 chunks per row (D = 128: four lanes, D = 64: eight), every lane receiving the sum.
@@ -37,14 +40,14 @@ __device__ __forceinline__ float chunk_sum(float x) {
   return quad_sum(x);
 }
 
-// One workgroup pools kPoolBlocks consecutive key blocks of one (batch, head), for K and V; each
-// wave takes kPoolPerWave of them.  A wave loads whole rows (lane l: 16-byte chunk l % C of rows
+// One workgroup pools BLOCKS consecutive key blocks of one (batch, head), for K and V; each wave
+// takes BLOCKS / kPoolWaves of them.  A wave loads whole rows (lane l: 16-byte chunk l % C of rows
 // l / C, l / C + 64 / C, ...), keeps fp32 sums of its chunk, and combines the lanes that share a
 // chunk with cross-lane operations (fixed order: deterministic).  The mean divides by n_j.  Vbar^T
-// is staged in LDS and written as one 2 x kPoolBlocks-byte run per head-dimension row.  K and V
+// is staged in LDS and written as one 2 x BLOCKS-byte run per head-dimension row.  K and V
 // are streamed with non-temporal loads (each byte is read once; the attention kernel that follows
 // reads the heads again from the first, long after these lines would have left the caches).
-template <int D>
+template <int D, int BLOCKS>
 __global__ __launch_bounds__(64 * kPoolWaves) void pool_kv_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, Strides kv, int64_t N, int block,
     int64_t M, int64_t Mp, float* __restrict__ kbar, float* __restrict__ vbar,
@@ -52,7 +55,8 @@ __global__ __launch_bounds__(64 * kPoolWaves) void pool_kv_kernel(
   constexpr int C = D / 8;           // 16-byte chunks per row
   constexpr int RS = 64 / C;         // rows per wave load instruction
   constexpr int U = 8;               // row sets in flight per tensor
-  __shared__ __attribute__((aligned(16))) uint16_t vt[D][kPoolBlocks];
+  constexpr int kPerWave = BLOCKS / kPoolWaves;
+  __shared__ __attribute__((aligned(16))) uint16_t vt[D][BLOCKS];
   const int64_t bh = blockIdx.y;
   const int64_t BH = gridDim.y;
   const int lane = threadIdx.x & 63;
@@ -61,9 +65,9 @@ __global__ __launch_bounds__(64 * kPoolWaves) void pool_kv_kernel(
   const uint16_t* kb = k + kv.base(bh);
   const uint16_t* vb = v + kv.base(bh);
   const int64_t jlast = (kp || vbt) ? Mp : M;  // blocks written (padding blocks: zeros)
-  for (int bl = 0; bl < kPoolPerWave; ++bl) {
-    const int jl = wave * kPoolPerWave + bl;  // block within the group
-    const int64_t j = (int64_t)blockIdx.x * kPoolBlocks + jl;
+  for (int bl = 0; bl < kPerWave; ++bl) {
+    const int jl = wave * kPerWave + bl;  // block within the group
+    const int64_t j = (int64_t)blockIdx.x * BLOCKS + jl;
     if (j >= jlast) break;
     float sk[8], sv[8];
 #pragma unroll
@@ -146,10 +150,10 @@ __global__ __launch_bounds__(64 * kPoolWaves) void pool_kv_kernel(
   }
   if (vbt) {
     __syncthreads();
-    // row d of the group's Vbar^T tile: kPoolBlocks bf16 = 4 chunks of 16 bytes
-    const int64_t j0 = (int64_t)blockIdx.x * kPoolBlocks;
-    for (int i = threadIdx.x; i < D * (kPoolBlocks / 8); i += 64 * kPoolWaves) {
-      const int d = i / (kPoolBlocks / 8), ch = i % (kPoolBlocks / 8);
+    // row d of the group's Vbar^T tile: BLOCKS bf16 = BLOCKS / 8 chunks of 16 bytes
+    const int64_t j0 = (int64_t)blockIdx.x * BLOCKS;
+    for (int i = threadIdx.x; i < D * (BLOCKS / 8); i += 64 * kPoolWaves) {
+      const int d = i / (BLOCKS / 8), ch = i % (BLOCKS / 8);
       if (j0 + ch * 8 < Mp)
         *reinterpret_cast<u32x4*>(vbt + (bh * D + d) * Mp + j0 + ch * 8) =
             *reinterpret_cast<const u32x4*>(&vt[d][ch * 8]);
@@ -353,15 +357,17 @@ hipError_t launch_pool(int d, int64_t BH, int64_t N, int block, const void* k, c
                        hipStream_t stream) {
   const int64_t M = (N + block - 1) / block;
   const int64_t nb = (kp || vbt) ? Mp : M;
-  dim3 grid((unsigned)((nb + kPoolBlocks - 1) / kPoolBlocks), (unsigned)BH);
+  const bool small = BH * ((nb + kPoolBlocks - 1) / kPoolBlocks) < kPoolMinGroups;
+  const int per = small ? kPoolBlocksSmall : kPoolBlocks;
+  dim3 grid((unsigned)((nb + per - 1) / per), (unsigned)BH);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(64 * kPoolWaves), 0, stream, (const uint16_t*)k,
+                       (const uint16_t*)v, kv, N, block, M, Mp, kbar, vbar, kp, vbt);
+  };
   if (d == 64)
-    hipLaunchKernelGGL(pool_kv_kernel<64>, grid, dim3(64 * kPoolWaves), 0, stream,
-                       (const uint16_t*)k, (const uint16_t*)v, kv, N, block, M, Mp, kbar, vbar, kp,
-                       vbt);
+    small ? go(pool_kv_kernel<64, kPoolBlocksSmall>) : go(pool_kv_kernel<64, kPoolBlocks>);
   else
-    hipLaunchKernelGGL(pool_kv_kernel<128>, grid, dim3(64 * kPoolWaves), 0, stream,
-                       (const uint16_t*)k, (const uint16_t*)v, kv, N, block, M, Mp, kbar, vbar, kp,
-                       vbt);
+    small ? go(pool_kv_kernel<128, kPoolBlocksSmall>) : go(pool_kv_kernel<128, kPoolBlocks>);
   return hipGetLastError();
 }
 

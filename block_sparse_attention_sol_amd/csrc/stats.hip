@@ -25,11 +25,13 @@ namespace solattn {
 namespace {
 // Row statistics: eight waves of 32 rows share the staged covariance pieces (two waves per SIMD
 // hide each other's latency; the pieces' 96 KB of LDS at d = 128 allow one workgroup per CU),
-// over kRowStatsPasses passes of 256 rows.
+// over up to kRowStatsPasses passes of 256 rows: fewer when that leaves too few workgroups to
+// spread over the CUs (small heads), since each pass after the first reuses the staged pieces.
 constexpr int kRowStatsWaves = 8;
 constexpr int kRowStatsThreads = 64 * kRowStatsWaves;
 constexpr int kRowStatsRows = 32 * kRowStatsWaves;  // rows per pass
 constexpr int kRowStatsPasses = 8;
+constexpr int64_t kRowStatsMinGroups = 512;         // workgroups wanted before passes grow
 }  // namespace
 
 // ---------------------------------------------------------------------------------------------
@@ -37,11 +39,11 @@ constexpr int kRowStatsPasses = 8;
 // ---------------------------------------------------------------------------------------------
 
 template <int D>
-__global__ __launch_bounds__(kRowStatsThreads) void rowstats_kernel(RowStatsArgs a) {
+__global__ __launch_bounds__(kRowStatsThreads) void rowstats_kernel(RowStatsArgs a, int passes) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   lds_u8* smem = (lds_u8*)smem_raw;
-  constexpr int64_t kGroupRows = (int64_t)kRowStatsRows * kRowStatsPasses;
-  const int64_t groups = (a.N + kGroupRows - 1) / kGroupRows;
+  const int64_t group_rows = (int64_t)kRowStatsRows * passes;
+  const int64_t groups = (a.N + group_rows - 1) / group_rows;
   const int64_t bh = blockIdx.x / groups;
   const int64_t grp = blockIdx.x % groups;
   const int lane = threadIdx.x & 63, c = lane & 31, h = lane >> 5;
@@ -68,8 +70,8 @@ __global__ __launch_bounds__(kRowStatsThreads) void rowstats_kernel(RowStatsArgs
   // offset = p D D 2 + ab 32 2D + (crel ^ (kk << 5)).
   const int crel = c * (2 * D) + (swz<D>(c, h) << 4);
   const uint16_t* qhead = a.q + a.qs.base(bh);
-  for (int pp = 0; pp < kRowStatsPasses; ++pp) {
-    const int64_t r0 = grp * kGroupRows + (int64_t)pp * kRowStatsRows;
+  for (int pp = 0; pp < passes; ++pp) {
+    const int64_t r0 = grp * group_rows + (int64_t)pp * kRowStatsRows;
     if (r0 >= a.N) break;
     const int64_t row0w = r0 + wave * 32;  // this wave's first row
     const int64_t row = row0w + c;
@@ -191,9 +193,14 @@ static hipError_t launch_rowstats_t(const RowStatsArgs& a, hipStream_t stream) {
   auto kern = rowstats_kernel<D>;
   hipError_t err = set_smem(kern, smem);
   if (err != hipSuccess) return err;
-  constexpr int64_t kGroupRows = (int64_t)kRowStatsRows * kRowStatsPasses;
-  const int64_t groups = (a.N + kGroupRows - 1) / kGroupRows;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(a.BH * groups)), dim3(kRowStatsThreads), smem, stream, a);
+  // passes per workgroup: as many as keep at least kRowStatsMinGroups workgroups, 1 .. 8
+  const int64_t units = a.BH * ((a.N + kRowStatsRows - 1) / kRowStatsRows);
+  const int64_t want = (units + kRowStatsMinGroups - 1) / kRowStatsMinGroups;
+  const int passes = (int)(want < 1 ? 1 : want > kRowStatsPasses ? kRowStatsPasses : want);
+  const int64_t group_rows = (int64_t)kRowStatsRows * passes;
+  const int64_t groups = (a.N + group_rows - 1) / group_rows;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(a.BH * groups)), dim3(kRowStatsThreads), smem, stream, a,
+                     passes);
   return hipGetLastError();
 }
 
