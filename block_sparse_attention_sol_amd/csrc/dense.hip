@@ -9,6 +9,136 @@
 
 namespace solattn {
 
+// ---------------------------------------------------------------------------------------------
+// Software-pipelined exact loop, in steps of 32 keys (half a 64-key stage).  A wave keeps two
+// score blocks live: while the matrix cores compute S^T of the next 32 keys (phase A), the vector
+// ALU turns the current 32 keys' scores into probabilities; while the matrix cores accumulate
+// O^T += V^T P^T for the current 32 keys (phase B), the vector ALU takes the next block's row
+// maximum.  K and V tiles are double buffered separately, each with its own barrier, so the next
+// stage's keys can be in use while this stage's values still are.  The sched_group_barrier
+// pattern asks for vector work behind every MFMA; the compiler still moves phase A's probabilities
+// below the partial-block branch, after the S^T chain.  Pinning them behind each MFMA measured no
+// faster: with two waves per SIMD, the other wave fills what one in-order wave leaves idle.
+// ---------------------------------------------------------------------------------------------
+constexpr int kSgValu = 0x002 | 0x400;  // vector and transcendental instructions
+
+// Phase A: (QK) sn = S^T of the 32 keys at rows kr0.. of ktile, and the probabilities of the
+// current block sc (offset moff = -running max, or -inf for rows that do not take part) packed
+// into pk, with their rounded sum added to ps.
+template <int D, bool QK>
+__device__ __forceinline__ void phase_a(const lds_u8* ktile, int kr0, const bf16x8 (&qf)[D / 16],
+                                        f32x16& sn, const f32x16& sc, float sl2, float moff,
+                                        uint32_t (&pk)[8], float& ps) {
+  constexpr int NM = D / 16;        // MFMAs
+  constexpr int PER = 16 / NM;      // probabilities per MFMA slot (even)
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 31, h = lane >> 5;
+  if constexpr (QK) sn = f32x16{};
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    if constexpr (QK) {
+      const u32x4 raw = lds_read16(ktile + tile_off<D>(kr0 + c, 2 * i + h));
+      sn = mfma32(__builtin_bit_cast(bf16x8, raw), qf[i], sn);
+    }
+#pragma unroll
+    for (int u = 0; u < PER; u += 2) {
+      const int v = i * PER + u;
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[v], sl2, moff));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[v + 1], sl2, moff));
+      pk[v / 2] = pack_bf16x2(p0, p1);
+      ps = add_bf16x2(pk[v / 2], ps);
+    }
+  }
+  if constexpr (QK) {
+    // K operand reads run three MFMAs ahead
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 3, 0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i + 3 < NM) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgValu, 3 * PER, 0);
+    }
+  }
+}
+
+// Phase B: O^T += V^T P^T for the 32 keys at rows vr0.. of vtile and, when MX, the maximum of the
+// next block's scores sn (raw, before scaling).
+template <int D, bool MX>
+__device__ __forceinline__ float phase_b(const lds_u8* vtile, int vr0, const uint32_t (&pk)[8],
+                                         const f32x16& sn, f32x16 (&o)[D / 32]) {
+  constexpr int NM = 2 * (D / 32);  // MFMAs
+  constexpr int PER = 16 / NM;      // maxima per MFMA slot
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4, j = lane & 15;
+  const int h = grp >> 1, cg = grp & 1;
+  float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+  for (int e2 = 0; e2 < 2; ++e2) {
+    const bf16x8 b = p_operand(pk, e2);
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds) {
+      const int d0 = 32 * ds + 16 * cg + 4 * (j & 3);
+      s16x4 x[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int row = vr0 + 16 * e2 + 8 * r + 4 * h + (j >> 2);
+        const lds_u8* p = vtile + tile_off<D>(row, d0 >> 3) + ((d0 >> 2) & 1) * 8;
+        x[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(p));
+      }
+      u32x4 raw;
+      raw[0] = __builtin_bit_cast(u32x2, x[0])[0];
+      raw[1] = __builtin_bit_cast(u32x2, x[0])[1];
+      raw[2] = __builtin_bit_cast(u32x2, x[1])[0];
+      raw[3] = __builtin_bit_cast(u32x2, x[1])[1];
+      o[ds] = mfma32(__builtin_bit_cast(bf16x8, raw), b, o[ds]);
+      if constexpr (MX) {
+        const int step = e2 * (D / 32) + ds;
+#pragma unroll
+        for (int u = 0; u < PER; u += 2) {
+          m0 = fmaxf(m0, sn[step * PER + u]);
+          m1 = fmaxf(m1, sn[step * PER + u + 1]);
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    if (i + 2 < NM) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    if constexpr (MX) __builtin_amdgcn_sched_group_barrier(kSgValu, PER, 0);
+  }
+  return fmaxf(m0, m1);
+}
+
+// Keys of a 32-key block at or beyond nvalid (counted from the block's first key) get -inf.
+__device__ __forceinline__ void mask_tail(f32x16& s, int nvalid) {
+  const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+    if (key_of(v, h) >= nvalid) s[v] = -INFINITY;
+}
+
+// Raise the running max to the block maximum mt_raw (raw score units) when it exceeds it by more
+// than kSlack, rescaling the accumulators; rows that do not take part never raise it.
+template <int D>
+__device__ __forceinline__ void raise_max(float mt_raw, bool active, float sl2, float& mrun,
+                                          float& lsum, f32x16 (&o)[D / 32]) {
+  const float mt = pair_max(mt_raw) * sl2;
+  const bool grow = active && mt > mrun + kSlack;
+  if (__builtin_amdgcn_ballot_w64(grow)) {
+    const float mnew = grow ? mt : mrun;
+    const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+    mrun = mnew;
+    lsum *= alpha;
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[ds][v] *= alpha;
+  }
+}
+
 // Half HB of stage n of the pipelined exact loop over consecutive stages (dense kernel); B = n & 1.
 // NEXT: a next 32-key block exists (it may be partial).  sc holds the current block's scores,
 // sn receives the next block's.  K tiles live at kbuf + b * tile, V tiles at vbuf + b * tile.
