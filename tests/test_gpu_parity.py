@@ -51,6 +51,7 @@ def _log(msg):
 @pytest.mark.parametrize("N,d,block", [(1024, 64, 64), (1000, 128, 128), (333, 64, 128), (1, 128, 64),
                                        (75600, 128, 128)])
 def test_pool_kv(sol, N, d, block):
+    """Two heads: few enough workgroups that the pooling kernel takes 8 blocks per workgroup."""
     _log(f"pool N={N} d={d} block={block}")
     q, k, v = _qkv(1, 2, N, d, seed=N + d)
     kbar, vbar = sol.pool_kv(k, v, block)
@@ -60,6 +61,18 @@ def test_pool_kv(sol, N, d, block):
         rv = oracle.pool(_np(v[0, h]), block)
         assert np.abs(kbar[0, h].cpu().numpy() - rk).max() <= 1e-5
         assert np.abs(vbar[0, h].cpu().numpy() - rv).max() <= 1e-5
+
+
+def test_pool_kv_many_heads(sol):
+    """64 heads x 256 blocks: 512 groups of 32 blocks, so the pooling kernel takes 32 blocks per
+    workgroup (the Wan-shape test below covers the same split at d = 128)."""
+    _log("pool many heads N=16384 d=64 block=64")
+    q, k, v = _qkv(1, 64, 16384, 64, seed=99)
+    kbar, vbar = sol.pool_kv(k, v, 64)
+    torch.cuda.synchronize()
+    for h in (0, 31, 63):
+        assert np.abs(kbar[0, h].cpu().numpy() - oracle.pool(_np(k[0, h]), 64)).max() <= 1e-5
+        assert np.abs(vbar[0, h].cpu().numpy() - oracle.pool(_np(v[0, h]), 64)).max() <= 1e-5
 
 
 # ------------------------------------------------------------------------------------------------
@@ -287,6 +300,17 @@ def test_wan_workload_full_shape(sol, wan_inputs, beta):
     _log(f"wan beta={beta}")
     _sparse_vs_oracle(sol, q, k, v, beta, 128, rows_per_head=400, heads=[0, 17, 39],
                       what=f"wan beta={beta}", full_mask_heads=[0, 39])
+
+
+def test_wan_pool_full_shape(sol, wan_inputs):
+    """Pooling at the Wan2.1-14B shape (40 heads x 19 groups of 32 blocks, last block 80 tokens)."""
+    q, k, v = wan_inputs
+    _log("wan pool")
+    kbar, vbar = sol.pool_kv(k, v, 128)
+    torch.cuda.synchronize()
+    for h in (0, 39):
+        assert np.abs(kbar[0, h].cpu().numpy() - oracle.pool(_np(k[0, h]), 128)).max() <= 1e-5
+        assert np.abs(vbar[0, h].cpu().numpy() - oracle.pool(_np(v[0, h]), 128)).max() <= 1e-5
 
 
 def test_wan_dense_full_shape(sol, wan_inputs):
