@@ -203,9 +203,17 @@ namespace {
 int attn_forward(const sol_shape* shape, const sol_strides* in_st, const sol_strides* out_st,
                  const void* q, const void* k, const void* v, float beta, int block, void* out,
                  void* workspace, size_t workspace_bytes, const sol_attn_debug* dbg,
-                 const uint32_t* mask_in, int drop_in, void* stream) {
+                 const uint32_t* mask_in, int drop_in, void* stream,
+                 const sol_grid* grid = nullptr) {
   int st;
   if ((st = check_shape(shape)) || (st = check_block(block))) return st;
+  if (grid) {
+    const int64_t N = shape->N;
+    if (grid->T < 1 || grid->H < 1 || grid->W < 1 || grid->T > N || grid->H > N || grid->W > N ||
+        grid->T * grid->H > N || grid->T * grid->H * grid->W != N)
+      return fail(SOL_EINVAL, "grid %lld x %lld x %lld does not hold N = %lld tokens",
+                  (long long)grid->T, (long long)grid->H, (long long)grid->W, (long long)N);
+  }
   if ((st = check_strides(*shape, in_st, "input", false)) ||
       (st = check_strides(*shape, out_st, "output", true)))
     return st;
@@ -302,15 +310,27 @@ int attn_forward(const sol_shape* shape, const sol_strides* in_st, const sol_str
   a.Mp = Mp;
   a.block = block;
   a.drop = drop_in;
+  // the latent grid regroups the 16-row segments of the d = 128 kernel (whole segments per row)
+  const bool grouped = grid && d == 128 && grid->W % 16 == 0;
+  if (grouped) {
+    a.gT = grid->T;
+    a.gH = grid->H;
+    a.gS = grid->W / 16;
+  }
   if (dbg) {
     if (!mask_in) a.drop = dbg->drop_unselected ? 1 : 0;
     a.lse = dbg->lse;
-    a.tile_kept = dbg->tile_kept;
+    a.tile_kept = grouped ? nullptr : dbg->tile_kept;
     a.out_f32 = dbg->out_f32;
   }
   e = solattn::launch_sparse(d, a, s);
   if (e != hipSuccess) return hip_status(e, "sparse attention kernel launch");
-  return hip_status(mark(3), "event record");
+  if ((e = mark(3)) != hipSuccess) return hip_status(e, "event record");
+  if (grouped && dbg && dbg->tile_kept) {  // contiguous-tile unions, after the timed kernels
+    e = solattn::launch_tile_union(BH, shape->N, Mp / 32, rowmask, dbg->tile_kept, s);
+    if (e != hipSuccess) return hip_status(e, "tile union launch");
+  }
+  return SOL_OK;
 }
 
 }  // namespace
@@ -320,6 +340,14 @@ int sol_attn_fwd_ex(const sol_shape* shape, const void* q, const void* k, const 
                     const sol_attn_debug* dbg, void* stream) {
   return attn_forward(shape, nullptr, nullptr, q, k, v, beta, block, out, workspace,
                       workspace_bytes, dbg, nullptr, 0, stream);
+}
+
+int sol_attn_fwd_grid(const sol_shape* shape, const sol_grid* grid, const void* q, const void* k,
+                      const void* v, float beta, int block, void* out, void* workspace,
+                      size_t workspace_bytes, const sol_attn_debug* dbg, void* stream) {
+  if (!grid) return fail(SOL_EINVAL, "grid is NULL");
+  return attn_forward(shape, nullptr, nullptr, q, k, v, beta, block, out, workspace,
+                      workspace_bytes, dbg, nullptr, 0, stream, grid);
 }
 
 int sol_attn_fwd_strided(const sol_shape* shape, const sol_strides* in_strides,

@@ -554,6 +554,31 @@ __device__ __forceinline__ void epilogue16(const f32x4 (&o)[D / 16], float mrun,
   }
 }
 
+// First row of the 16-row query segment at position p of the workgroup order (workgroup tile,
+// wave w: p = kWaves16 * tile + w).  Without a latent grid (gS = 0) the rows are consecutive.
+// With a grid of T frames, H rows and S segments of 16 tokens per row, positions run over blocks
+// of 2 frames x 4 rows (smaller at the last frame pair and the last rows of a frame), and inside
+// a block over the segment's horizontal position, then the row, then the frame: eight
+// consecutive positions cover 2 frames x 4 rows at one horizontal position, rows whose selections
+// overlap more than those of 128 consecutive rows.  Positions past the last segment give N.
+__device__ __forceinline__ int64_t seg_row(const SparseArgs& a, int64_t p) {
+  if (a.gS == 0) return p * 16;
+  const uint32_t T = (uint32_t)a.gT, H = (uint32_t)a.gH, S = (uint32_t)a.gS;
+  if (p >= (int64_t)T * H * S) return a.N;
+  const uint32_t pp = (uint32_t)p;
+  const uint32_t per_pair = 2u * H * S;
+  const uint32_t tp = pp / per_pair;                              // frame pair
+  const uint32_t p1 = pp - tp * per_pair;
+  const uint32_t tq = T - 2u * tp < 2u ? T - 2u * tp : 2u;        // frames in the pair
+  const uint32_t yq = p1 / (4u * S * tq);                         // row quad
+  const uint32_t r = p1 - yq * 4u * S * tq;
+  const uint32_t yn = H - 4u * yq < 4u ? H - 4u * yq : 4u;        // rows in the quad
+  const uint32_t xs = r / (yn * tq);                              // horizontal segment
+  const uint32_t rem = r - xs * yn * tq;
+  const uint32_t yy = rem / tq, tt = rem - yy * tq;
+  return ((int64_t)((2u * tp + tt) * H + 4u * yq + yy) * S + xs) * 16;
+}
+
 template <int D, int BLK>
 __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a) {
   static_assert(D == 128, "the 16-row kernel serves head dimension 128");
@@ -579,7 +604,7 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
   if (!work_item(a.BH * ntiles, w)) return;
   const int64_t bh = w / ntiles;
   const int64_t tile = w % ntiles;
-  const int64_t row0 = tile * QT + wave * 16;  // first row of this wave
+  const int64_t row0 = seg_row(a, tile * kWaves16 + wave);  // first row of this wave
   const int64_t row = row0 + q;
   const bool rvalid = row < a.N;
 
@@ -900,7 +925,9 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
     dcur = dnxt;
     dnxt = dnn;
   }
-  if (a.tile_kept && wave == 0) {  // blocks kept by some row of the tile
+  // blocks kept by some row of the tile (with a latent grid the workgroup's rows are not a
+  // contiguous tile: tile_union_kernel fills tile_kept instead)
+  if (a.tile_kept && a.gS == 0 && wave == 0) {
     int kept = 0;
     for (int i = 0; i < W; ++i)
       kept += __builtin_popcount(union_of_waves(lane < kWaves16 ? wmask[lane * W + i] : 0u));
@@ -946,6 +973,33 @@ static hipError_t launch_sparse16_t(const SparseArgs& a, hipStream_t stream) {
   if (err != hipSuccess) return err;
   const int64_t ntiles = (a.N + kQTile - 1) / kQTile;
   hipLaunchKernelGGL(kern, dim3(xcd_grid(a.BH * ntiles)), dim3(kThreads16), smem, stream, a);
+  return hipGetLastError();
+}
+
+// tile_kept of the debug outputs when the fused kernel's workgroups are not contiguous tiles: one
+// wave per (head, 128-row tile) ORs the tile's selection words, word by word, and counts the bits.
+__global__ __launch_bounds__(64) void tile_union_kernel(const uint32_t* __restrict__ rowmask,
+                                                        int64_t N, int64_t W, int64_t ntiles,
+                                                        int32_t* __restrict__ tile_kept) {
+  const int64_t bh = blockIdx.x / ntiles, t = blockIdx.x % ntiles;
+  const int lane = threadIdx.x;
+  const uint32_t* rm = rowmask + bh * W * N;
+  const int64_t r0 = t * kQTile + lane, r1 = r0 + 64;
+  int kept = 0;
+  for (int64_t w = 0; w < W; ++w) {
+    uint32_t x = (r0 < N ? rm[w * N + r0] : 0u) | (r1 < N ? rm[w * N + r1] : 0u);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x |= (uint32_t)__shfl_xor((int)x, o);
+    kept += __builtin_popcount(x);
+  }
+  if (lane == 0) tile_kept[bh * ntiles + t] = kept;
+}
+
+hipError_t launch_tile_union(int64_t BH, int64_t N, int64_t W, const uint32_t* rowmask,
+                             int32_t* tile_kept, hipStream_t stream) {
+  const int64_t ntiles = (N + kQTile - 1) / kQTile;
+  hipLaunchKernelGGL(tile_union_kernel, dim3((unsigned)(BH * ntiles)), dim3(64), 0, stream, rowmask,
+                     N, W, ntiles, tile_kept);
   return hipGetLastError();
 }
 

@@ -56,6 +56,9 @@ struct SparseArgs {
   int block;
   int drop;
   const uint32_t* mask_in;  // [BH][N][Mp/32] caller's selection (replaces s >= tau), or NULL
+  // latent grid of the query rows (frames, rows, 16-token segments per row) for the grouping of
+  // 16-row segments into workgroups; gS = 0: consecutive rows (the only grouping at d = 64)
+  int64_t gT, gH, gS;
   // optional outputs
   uint32_t* mask_out;   // [BH][N][Mp/32] selection words, row-major
   float* lse;
@@ -63,6 +66,10 @@ struct SparseArgs {
   float* out_f32;
 };
 hipError_t launch_sparse(int d, const SparseArgs& a, hipStream_t stream);
+// tile_kept[bh][t] = key blocks kept by some row of contiguous 128-row tile t, from the routing
+// sweep's selection words rowmask [BH][W][N] (W = Mp / 32)
+hipError_t launch_tile_union(int64_t BH, int64_t N, int64_t W, const uint32_t* rowmask,
+                             int32_t* tile_kept, hipStream_t stream);
 
 hipError_t launch_dense(int d, int64_t BH, int64_t N, const void* q, const void* k, const void* v,
                         const Strides& in, void* out, const Strides& outs, float* lse,

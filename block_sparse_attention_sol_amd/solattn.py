@@ -27,6 +27,7 @@ EXPORTS = (
     "sol_pool_kv",
     "sol_attn_fwd",
     "sol_attn_fwd_ex",
+    "sol_attn_fwd_grid",
     "sol_attn_fwd_noalloc",
     "sol_attn_fwd_masked",
     "sol_proxy_map",
@@ -49,6 +50,10 @@ class SolShape(ctypes.Structure):
 
 class SolStrides(ctypes.Structure):
     _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("n", ctypes.c_int64)]
+
+
+class SolGrid(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int64), ("W", ctypes.c_int64)]
 
 
 class SolAttnDebug(ctypes.Structure):
@@ -87,6 +92,8 @@ def load_library(path: str = LIB_PATH):
     lib.sol_attn_fwd_ex.argtypes = [shp, vp, vp, vp, cf, ci, vp, vp, sz,
                                     ctypes.POINTER(SolAttnDebug), vp]
     lib.sol_attn_fwd_noalloc.argtypes = [shp, vp, vp, vp, cf, ci, vp, vp]
+    lib.sol_attn_fwd_grid.argtypes = [shp, ctypes.POINTER(SolGrid), vp, vp, vp, cf, ci, vp, vp, sz,
+                                      ctypes.POINTER(SolAttnDebug), vp]
     lib.sol_dense_fwd.argtypes = [shp, vp, vp, vp, vp, vp, vp]
     lib.sol_mfma_probe.argtypes = [ci, ci, vp, vp]
     stp = ctypes.POINTER(SolStrides)
@@ -185,9 +192,11 @@ def pool_kv(k, v, block: int, stream=None):
 
 
 def attn_fwd(q, k, v, beta: float, block: int, out=None, workspace=None, debug: bool = False,
-             drop_unselected: bool = False, events=None, stream=None):
+             drop_unselected: bool = False, events=None, stream=None, grid=None):
     """Sol-Attn forward.  Returns out, or (out, dict of debug outputs) when debug/drop/events is
-    set.  events: 4 raw hipEvent_t handles recorded at the kernel boundaries (see HipEvents)."""
+    set.  events: 4 raw hipEvent_t handles recorded at the kernel boundaries (see HipEvents).
+    grid: the tokens' latent grid (T, H, W), passed to sol_attn_fwd_grid (same results; the
+    fused kernel groups query rows by it)."""
     import torch
     lib = load_library()
     B, H, N, d = q.shape
@@ -202,7 +211,7 @@ def attn_fwd(q, k, v, beta: float, block: int, out=None, workspace=None, debug: 
         workspace = new_workspace(q.shape, block, q.device)
     shp = _shape(q)
     if _strided_call(q, k, v, out):
-        if debug or drop_unselected or events is not None:
+        if debug or drop_unselected or events is not None or grid is not None:
             raise ValueError("debug outputs, the drop ablation and events need contiguous tensors")
         _check(lib.sol_attn_fwd_strided(ctypes.byref(shp), ctypes.byref(_strides(q)),
                                         ctypes.byref(_strides(out)), _dev(q, "q", True),
@@ -210,7 +219,7 @@ def attn_fwd(q, k, v, beta: float, block: int, out=None, workspace=None, debug: 
                                         _dev(out, "out", True), _dev(workspace, "workspace"),
                                         workspace.numel(), _stream(stream)))
         return out
-    if not debug and not drop_unselected and events is None:
+    if not debug and not drop_unselected and events is None and grid is None:
         _check(lib.sol_attn_fwd(ctypes.byref(shp), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
                                 float(beta), block, _dev(out, "out"), _dev(workspace, "workspace"),
                                 workspace.numel(), _stream(stream)))
@@ -237,6 +246,15 @@ def attn_fwd(q, k, v, beta: float, block: int, out=None, workspace=None, debug: 
     if events is not None:
         for i, e in enumerate(events):
             dstruct.events[i] = e
+    if grid is not None:
+        g = SolGrid(*[int(x) for x in grid])
+        _check(lib.sol_attn_fwd_grid(ctypes.byref(shp), ctypes.byref(g), _dev(q, "q"),
+                                     _dev(k, "k"), _dev(v, "v"), float(beta), block,
+                                     _dev(out, "out"), _dev(workspace, "workspace"),
+                                     workspace.numel(), ctypes.byref(dstruct), _stream(stream)))
+        if not debug and not drop_unselected and events is None:
+            return out
+        return out, dbg
     _check(lib.sol_attn_fwd_ex(ctypes.byref(shp), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
                                float(beta), block, _dev(out, "out"), _dev(workspace, "workspace"),
                                workspace.numel(), ctypes.byref(dstruct), _stream(stream)))

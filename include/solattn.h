@@ -24,7 +24,8 @@
  *   Scale     1/sqrt(d), fixed.
  *   Supported d in {64, 128}; block in {64, 128}; 1 <= N <= 2^22; 1 <= B*H <= 65535.
  *   Pointers  all tensor pointers are device pointers, 16-byte aligned, owned by the caller.
- *             The library never allocates or frees device memory and keeps no device state.
+ *             The library never allocates or frees device memory and keeps no device state
+ *             (apart from the fixed scratch array of sol_attn_fwd_noalloc, see there).
  *             out must not overlap q, k, v or the workspace.
  *   Streams   `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every call only
  *             enqueues work on that stream and returns; nothing synchronises.  A fault inside a
@@ -106,7 +107,9 @@ typedef struct sol_attn_debug {
   float* sigma;        /* [B][H][N] row population standard deviation */
   float* tau;          /* [B][H][N] threshold mu + beta*sigma (+-inf for infinite beta) */
   float* lse;          /* [B][H][N] natural log of the softmax denominator (with its max) */
-  int32_t* tile_kept;  /* [B][H][ceil(N/SOL_QUERY_TILE)] key blocks computed for each query tile */
+  int32_t* tile_kept;  /* [B][H][ceil(N/SOL_QUERY_TILE)] key blocks kept by some row of each
+                          contiguous 128-row query tile (the blocks the fused kernel computes for
+                          that tile, unless a latent grid regroups the rows: sol_attn_fwd_grid) */
   float* out_f32;      /* [B][H][N][d] the output before its final rounding to bf16 (out is the
                           round-to-nearest-even bf16 of these values) */
   int drop_unselected; /* 0: the method.  1: ablation -- unselected blocks are dropped instead of
@@ -121,6 +124,29 @@ typedef struct sol_attn_debug {
 int sol_attn_fwd_ex(const sol_shape* shape, const void* q, const void* k, const void* v,
                     float beta, int block, void* out, void* workspace, size_t workspace_bytes,
                     const sol_attn_debug* dbg, void* stream);
+
+/* Latent grid of the tokens of a video DiT (the workloads of the page's results paragraph): T
+ * frames of H x W latent positions, token n at frame t, row y, column x with
+ * n = (t * H + y) * W + x. */
+typedef struct sol_grid {
+  int64_t T, H, W;
+} sol_grid;
+
+/*
+ * sol_attn_fwd_ex with the tokens' latent grid.  The grid changes only how the fused kernel
+ * groups query rows into workgroups, never what is computed: at d = 128 each workgroup takes
+ * eight 16-query row segments from 2 frames x 4 latent rows at one horizontal position (smaller
+ * groups at the grid's far edges are merged in order), instead of 128 consecutive rows.  Such
+ * rows keep similar key blocks, so the union of blocks a workgroup copies and computes is
+ * smaller.  Every row's selection, pooled tokens and exact blocks are the same as
+ * sol_attn_fwd_ex's; results agree up to fp32 summation order.  The debug outputs keep their
+ * meaning (tile_kept still counts the blocks kept by contiguous 128-row tiles).
+ * With d = 64, or W not a multiple of 16, the rows keep the contiguous grouping.
+ *   grid   T, H, W >= 1 and T * H * W == shape->N, else SOL_EINVAL.
+ */
+int sol_attn_fwd_grid(const sol_shape* shape, const sol_grid* grid, const void* q, const void* k,
+                      const void* v, float beta, int block, void* out, void* workspace,
+                      size_t workspace_bytes, const sol_attn_debug* dbg, void* stream);
 
 /*
  * sol_attn_fwd on strided views (no transposes needed in a transformer block): q, k and v share

@@ -165,6 +165,40 @@ def test_attn_fwd_noalloc_rejects(lib, case):
     assert lib.sol_last_error(), case
 
 
+@pytest.mark.parametrize("case", ["null_grid", "grid_too_small", "grid_too_large", "zero_t",
+                                  "negative_w", "huge_factor", "grid_ok_small_workspace"])
+def test_attn_fwd_grid_rejects(lib, case):
+    """The latent grid must hold exactly N tokens; it is checked with the other arguments, before
+    any HIP call."""
+    s = _shape()
+    q, k, v, out, ws = _ptrs(5)
+    need = lib.sol_attn_workspace_bytes(ctypes.byref(s), 128)
+    nbytes = need
+    g = solattn.SolGrid(2, 4, s.N // 8)
+    assert g.T * g.H * g.W == s.N
+    grid_arg = ctypes.byref(g)
+    expect = solattn.SOL_EINVAL
+    if case == "null_grid":
+        grid_arg = None
+    elif case == "grid_too_small":
+        g.W -= 1
+    elif case == "grid_too_large":
+        g.W += 1
+    elif case == "zero_t":
+        g.T = 0
+    elif case == "negative_w":
+        g.W = -g.W
+    elif case == "huge_factor":
+        g.T, g.H, g.W = 1 << 40, 1 << 40, 1
+    elif case == "grid_ok_small_workspace":
+        nbytes = need - 1
+        expect = solattn.SOL_EWORKSPACE
+    st = lib.sol_attn_fwd_grid(ctypes.byref(s), grid_arg, q, k, v, 0.5, 128, out, ws, nbytes, None,
+                               None)
+    assert st == expect, (case, st, lib.sol_last_error())
+    assert lib.sol_last_error(), case
+
+
 def test_noalloc_scratch_size_matches_header():
     text = open(HEADER).read()
     m = re.search(r"#define SOL_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)

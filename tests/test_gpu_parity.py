@@ -99,8 +99,8 @@ def test_dense(sol, B, H, N, d):
 # ------------------------------------------------------------------------------------------------
 
 def _sparse_vs_oracle(sol, q, k, v, beta, block, rows_per_head=None, heads=None, what="",
-                      full_mask_heads=()):
-    out, dbg = sol.attn_fwd(q, k, v, beta, block, debug=True)
+                      full_mask_heads=(), grid=None):
+    out, dbg = sol.attn_fwd(q, k, v, beta, block, debug=True, grid=grid)
     torch.cuda.synchronize()
     B, H, N, d = q.shape
     heads = range(H) if heads is None else heads
@@ -311,6 +311,54 @@ def test_wan_pool_full_shape(sol, wan_inputs):
     for h in (0, 39):
         assert np.abs(kbar[0, h].cpu().numpy() - oracle.pool(_np(k[0, h]), 128)).max() <= 1e-5
         assert np.abs(vbar[0, h].cpu().numpy() - oracle.pool(_np(v[0, h]), 128)).max() <= 1e-5
+
+
+@pytest.mark.parametrize("beta", [2.2, 1.0])
+def test_wan_workload_grid_grouping(sol, wan_inputs, beta):
+    """The Wan2.1-14B shape through sol_attn_fwd_grid (21 x 45 x 80 latent grid: the fused kernel
+    groups 2 frames x 4 rows x 16 tokens per workgroup).  Against the oracle as the contiguous
+    call is, and against the contiguous call itself: the selection masks and the contiguous-tile
+    unions are identical, the outputs differ only by summation order."""
+    q, k, v = wan_inputs
+    _log(f"wan grid beta={beta}")
+    out_g, dbg_g = _sparse_vs_oracle(sol, q, k, v, beta, 128, rows_per_head=400, heads=[0, 17, 39],
+                                     what=f"wan grid beta={beta}", full_mask_heads=[39],
+                                     grid=(21, 45, 80))
+    out_c, dbg_c = sol.attn_fwd(q, k, v, beta, 128, debug=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dbg_g["mask"], dbg_c["mask"])
+    assert torch.equal(dbg_g["tile_kept"], dbg_c["tile_kept"])
+    assert torch.equal(dbg_g["mu"], dbg_c["mu"]) and torch.equal(dbg_g["tau"], dbg_c["tau"])
+    # The two calls visit a row's blocks in different orders, so each probability is rounded to
+    # bf16 (the matrix product's operand) against a different running maximum: each call's output
+    # is within about 2^-9 of the largest value magnitude of the exact p-weighted mean of its
+    # rounded weights, so the two differ by at most 2^-8 of max|v| (plus fp32 summation order).
+    diff = (dbg_g["out_f32"] - dbg_c["out_f32"]).abs()
+    vmax = v.float().abs().amax(dim=(2, 3), keepdim=True)
+    _log(f"wan grid beta={beta}: max |grid - contiguous| {diff.max().item():.3e}, "
+         f"{(diff / vmax).max().item():.3e} of max|v|")
+    assert bool((diff <= vmax * 2.0 ** -8 + 1e-5).all())
+
+
+# Ragged latent grids (odd frame count, rows not a multiple of 4, a single frame) exercise the
+# smaller groups at the grid's edges; W not a multiple of 16 and d = 64 keep the contiguous grouping
+# (bit-identical to the plain call).
+@pytest.mark.parametrize("grid,d,block,beta", [((3, 5, 32), 128, 128, 0.7), ((5, 7, 48), 128, 64, 1.3),
+                                               ((1, 3, 16), 128, 128, 0.2), ((4, 9, 80), 128, 128, 1.8),
+                                               ((2, 3, 40), 128, 128, 0.9), ((3, 5, 32), 64, 64, 0.7)])
+def test_grid_grouping_ragged(sol, grid, d, block, beta):
+    T, Hg, W = grid
+    N = T * Hg * W
+    _log(f"grid {grid} N={N} d={d} block={block} beta={beta}")
+    q, k, v = _qkv(1, 3, N, d, seed=N + d + block, scale=1.2)
+    out_g, dbg_g = _sparse_vs_oracle(sol, q, k, v, beta, block, what=f"grid {grid} d{d}",
+                                     full_mask_heads=[0, 2], grid=grid)
+    out_c, dbg_c = sol.attn_fwd(q, k, v, beta, block, debug=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dbg_g["mask"], dbg_c["mask"])
+    assert torch.equal(dbg_g["tile_kept"], dbg_c["tile_kept"])
+    if d == 64 or W % 16:
+        assert torch.equal(out_g, out_c) and torch.equal(dbg_g["out_f32"], dbg_c["out_f32"])
 
 
 def test_wan_dense_full_shape(sol, wan_inputs):
