@@ -281,11 +281,11 @@ def routing_comparison(sol, w, q, k, v, ws, spec, steps=5, warmup=2):
 FUSED_SOURCES = ("attn.hip", "tiles.hpp", "common.hpp", "kernels.hpp")
 
 
-def recorded_traffic(kernel_sources, workload, beta):
+def recorded_traffic(kernel_sources, workload, beta, grid):
     """HBM bytes per launch of the fused kernel, as recorded from rocprofv3 FETCH_SIZE/WRITE_SIZE
     counters (scaled by a plain-copy calibration) in profiles/sol_attn_wan_hbm_traffic.md, or
-    None when the record is missing, is for another workload or beta, or the kernel's sources have
-    changed since the counters were taken."""
+    None when the record is missing, is for another workload, beta or row grouping (latent grid
+    or not), or the kernel's sources have changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "sol_attn_wan_hbm_traffic.md")
     if not os.path.exists(path):
@@ -295,6 +295,8 @@ def recorded_traffic(kernel_sources, workload, beta):
         if line.startswith("traffic-record:"):
             rec = json.loads(line.split(":", 1)[1])
     if rec is None or rec.get("workload") != workload or abs(rec.get("beta", 1e9) - beta) > 1e-3:
+        return None
+    if bool(rec.get("grid", False)) != grid:
         return None
     h = hashlib.sha256()
     for f in kernel_sources:
@@ -317,6 +319,9 @@ def main():
                     help="calibrate beta to this per-row kept density instead (the secondary "
                          "operating point)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-grid", action="store_true",
+                    help="call the fused pass without the workload's latent grid (query rows in "
+                         "contiguous 128-row workgroups) instead of sol_attn_fwd_grid")
     ap.add_argument("--ablation", default=None, metavar="BETAS",
                     help="comma-separated betas: run the drop-vs-approximate ablation instead of the "
                          "benchmark and print its JSON line")
@@ -397,7 +402,9 @@ def main():
         beta = calibrate_beta(sol, q, k, v, w.block, target, ws, out)
     else:
         beta = w.betas[0]
-    _, dbg = sol.attn_fwd(q, k, v, beta, w.block, out=out, workspace=ws, debug=True)
+    # the workload's latent grid: the fused kernel groups query rows by it (same results)
+    grid = None if args.no_grid else w.grid
+    _, dbg = sol.attn_fwd(q, k, v, beta, w.block, out=out, workspace=ws, debug=True, grid=grid)
     torch.cuda.synchronize()
     M = sol.n_blocks(N, w.block)
     T = (N + sol.QUERY_TILE - 1) // sol.QUERY_TILE
@@ -427,7 +434,7 @@ def main():
 
     def step(i):
         sol.attn_fwd(q, k, v, beta, w.block, out=out, workspace=ws,
-                     events=ev.handles[4 * i: 4 * i + 4])
+                     events=ev.handles[4 * i: 4 * i + 4], grid=grid)
         dense_start[i].record()
         sol.dense_fwd(q, k, v, out=dout)
         dense_end[i].record()
@@ -468,7 +475,7 @@ def main():
     min_bytes = 4.0 * B * H * N * d * 2
     traffic = recorded_traffic(
         [os.path.join(ROOT, "block_sparse_attention_sol_amd", "csrc", f)
-         for f in FUSED_SOURCES], w.name, beta)
+         for f in FUSED_SOURCES], w.name, beta, grid is not None)
     result = {
         "metric": METRIC,
         "value": F_tile / (t_sparse * 1e-3) / 1e12,
@@ -489,6 +496,9 @@ def main():
             "target_kept_block_density": None if args.row_target is not None else target,
             "target_row_density": args.row_target, "query_tile": sol.QUERY_TILE,
             "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)",
+            "row_grouping": "latent grid %dx%dx%d: 2 frames x 4 rows x 16 tokens per workgroup"
+                            % tuple(grid) if grid is not None and d == 128 and grid[2] % 16 == 0
+                            else "contiguous 128-row tiles",
         },
         "sparse_ms": t_sparse,
         "sparse_ms_median": med(sparse_ms),
