@@ -361,6 +361,20 @@ def test_grid_grouping_ragged(sol, grid, d, block, beta):
         assert torch.equal(out_g, out_c) and torch.equal(dbg_g["out_f32"], dbg_c["out_f32"])
 
 
+def test_grid_grouping_batch(sol):
+    """Two batch entries and a grid whose frame count is odd: every (batch, head) slice regroups
+    its own rows."""
+    grid = (5, 4, 32)
+    N = 5 * 4 * 32
+    q, k, v = _qkv(2, 2, N, 128, seed=321, scale=1.1)
+    _log(f"grid batch {grid}")
+    out_g, dbg_g = _sparse_vs_oracle(sol, q, k, v, 0.6, 128, what="grid batch", grid=grid)
+    out_c, dbg_c = sol.attn_fwd(q, k, v, 0.6, 128, debug=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dbg_g["mask"], dbg_c["mask"])
+    assert torch.equal(dbg_g["tile_kept"], dbg_c["tile_kept"])
+
+
 def test_wan_dense_full_shape(sol, wan_inputs):
     q, k, v = wan_inputs
     _log("wan dense")
