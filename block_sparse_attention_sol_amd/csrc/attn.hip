@@ -556,27 +556,25 @@ __device__ __forceinline__ void epilogue16(const f32x4 (&o)[D / 16], float mrun,
 
 // First row of the 16-row query segment at position p of the workgroup order (workgroup tile,
 // wave w: p = kWaves16 * tile + w).  Without a latent grid (gS = 0) the rows are consecutive.
-// With a grid of T frames, H rows and S segments of 16 tokens per row, positions run over blocks
-// of 2 frames x 4 rows (smaller at the last frame pair and the last rows of a frame), and inside
-// a block over the segment's horizontal position, then the row, then the frame: eight
-// consecutive positions cover 2 frames x 4 rows at one horizontal position, rows whose selections
-// overlap more than those of 128 consecutive rows.  Positions past the last segment give N.
+// With a grid of T frames, H rows and S segments of 16 tokens per row, positions run over pairs
+// of frames (the last one single when T is odd); inside a pair over the horizontal segment, then
+// the row, then the frame.  Eight consecutive positions then cover 2 frames x 4 rows at one
+// horizontal position (a workgroup at the end of a column takes the next column's first rows),
+// rows whose selections overlap more than those of 128 consecutive rows, and consecutive
+// workgroups are vertical neighbours.  Positions past the last segment give N.
 __device__ __forceinline__ int64_t seg_row(const SparseArgs& a, int64_t p) {
   if (a.gS == 0) return p * 16;
   const uint32_t T = (uint32_t)a.gT, H = (uint32_t)a.gH, S = (uint32_t)a.gS;
   if (p >= (int64_t)T * H * S) return a.N;
   const uint32_t pp = (uint32_t)p;
   const uint32_t per_pair = 2u * H * S;
-  const uint32_t tp = pp / per_pair;                              // frame pair
+  const uint32_t tp = pp / per_pair;                        // frame pair
   const uint32_t p1 = pp - tp * per_pair;
-  const uint32_t tq = T - 2u * tp < 2u ? T - 2u * tp : 2u;        // frames in the pair
-  const uint32_t yq = p1 / (4u * S * tq);                         // row quad
-  const uint32_t r = p1 - yq * 4u * S * tq;
-  const uint32_t yn = H - 4u * yq < 4u ? H - 4u * yq : 4u;        // rows in the quad
-  const uint32_t xs = r / (yn * tq);                              // horizontal segment
-  const uint32_t rem = r - xs * yn * tq;
-  const uint32_t yy = rem / tq, tt = rem - yy * tq;
-  return ((int64_t)((2u * tp + tt) * H + 4u * yq + yy) * S + xs) * 16;
+  const uint32_t tq = T - 2u * tp < 2u ? T - 2u * tp : 2u;  // frames in the pair
+  const uint32_t xs = p1 / (H * tq);                        // horizontal segment
+  const uint32_t r = p1 - xs * H * tq;
+  const uint32_t y = r / tq, tt = r - y * tq;               // row, frame within the pair
+  return ((int64_t)((2u * tp + tt) * H + y) * S + xs) * 16;
 }
 
 template <int D, int BLK>

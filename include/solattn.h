@@ -135,8 +135,9 @@ typedef struct sol_grid {
 /*
  * sol_attn_fwd_ex with the tokens' latent grid.  The grid changes only how the fused kernel
  * groups query rows into workgroups, never what is computed: at d = 128 each workgroup takes
- * eight 16-query row segments from 2 frames x 4 latent rows at one horizontal position (smaller
- * groups at the grid's far edges are merged in order), instead of 128 consecutive rows.  Such
+ * eight 16-query row segments from 2 frames x 4 latent rows at one horizontal position (a
+ * workgroup at the bottom of a column continues in the next one), instead of 128 consecutive
+ * rows.  Such
  * rows keep similar key blocks, so the union of blocks a workgroup copies and computes is
  * smaller.  Every row's selection, pooled tokens and exact blocks are the same as
  * sol_attn_fwd_ex's; results agree up to fp32 summation order.  The debug outputs keep their
