@@ -34,7 +34,12 @@
 //                    where it can be (the CU has one scalar unit): wave 0 alone walks the union
 //                    and publishes each stage as a word in an LDS ring, and the lowest wave
 //                    without math issues the whole next-stage copy.  Each tile's walk starts at
-//                    a point that lines up the tiles running together on an XCD.
+//                    a point that lines up the tiles running together on an XCD.  Given the
+//                    tokens' latent grid, a workgroup's eight 16-row segments come from 2 frames
+//                    x 4 latent rows instead of 128 consecutive rows (seg_row): rows that keep
+//                    similar blocks, so the union each workgroup copies is smaller.
+//   tile_union_kernel  the debug output tile_kept (blocks kept by each contiguous 128-row tile)
+//                    from the selection words, for launches whose workgroups are not such tiles.
 // The proxy map is never written to memory; only the optional debug outputs leave the kernel.
 #include "tiles.hpp"
 
