@@ -451,14 +451,16 @@ def test_determinism(sol):
     assert torch.equal(c, e)
 
 
-@pytest.mark.parametrize("N,d,block,beta", [(900, 64, 64, 0.2), (1000, 128, 128, 0.6),
-                                            (2100, 128, 128, 2.2), (777, 128, 64, 1.0)])
-def test_drop_ablation(sol, N, d, block, beta):
+@pytest.mark.parametrize("N,d,block,beta,grid", [(900, 64, 64, 0.2, None), (1000, 128, 128, 0.6, None),
+                                                 (2100, 128, 128, 2.2, None), (777, 128, 64, 1.0, None),
+                                                 (1920, 128, 128, 1.1, (3, 5, 128))])
+def test_drop_ablation(sol, N, d, block, beta, grid):
     """Dropping unselected blocks (ablation flag) matches the oracle's drop mode, through the
-    threshold path of both fused kernels (d = 64 and the 16-row kernel at d = 128)."""
-    _log(f"drop ablation N={N} d={d} block={block} beta={beta}")
+    threshold path of both fused kernels (d = 64 and the 16-row kernel at d = 128, the latter
+    also with the latent-grid grouping)."""
+    _log(f"drop ablation N={N} d={d} block={block} beta={beta} grid={grid}")
     q, k, v = _qkv(1, 2, N, d, seed=21 + N, scale=1.3)
-    out, _ = sol.attn_fwd(q, k, v, beta, block, drop_unselected=True)
+    out, _ = sol.attn_fwd(q, k, v, beta, block, drop_unselected=True, grid=grid)
     out2, dbg = sol.attn_fwd(q, k, v, beta, block, debug=True)
     torch.cuda.synchronize()
     for h in range(2):
