@@ -30,7 +30,7 @@ namespace {
 constexpr int kRowStatsWaves = 8;
 constexpr int kRowStatsThreads = 64 * kRowStatsWaves;
 constexpr int kRowStatsRows = 32 * kRowStatsWaves;  // rows per pass
-constexpr int kRowStatsPasses = 8;
+constexpr int kRowStatsPasses = 16;
 constexpr int64_t kRowStatsMinGroups = 512;         // workgroups wanted before passes grow
 }  // namespace
 
@@ -193,7 +193,7 @@ static hipError_t launch_rowstats_t(const RowStatsArgs& a, hipStream_t stream) {
   auto kern = rowstats_kernel<D>;
   hipError_t err = set_smem(kern, smem);
   if (err != hipSuccess) return err;
-  // passes per workgroup: as many as keep at least kRowStatsMinGroups workgroups, 1 .. 8
+  // passes per workgroup: as many as keep at least kRowStatsMinGroups workgroups, 1 .. 16
   const int64_t units = a.BH * ((a.N + kRowStatsRows - 1) / kRowStatsRows);
   const int64_t want = (units + kRowStatsMinGroups - 1) / kRowStatsMinGroups;
   const int passes = (int)(want < 1 ? 1 : want > kRowStatsPasses ? kRowStatsPasses : want);
