@@ -69,8 +69,10 @@ typedef struct sol_strides {
   int64_t b, h, n;
 } sol_strides;
 
-/* Query rows handled together by one tile of the fused kernel.  A key block is computed for a
- * tile when any row of the tile keeps it (rows that do not keep it are masked inside the tile). */
+/* Query rows handled together by one tile of the fused kernel: 128 consecutive rows (or, with
+ * sol_attn_fwd_grid at d = 128, eight 16-row segments of the latent grid).  A key block is
+ * computed for a tile when any row of the tile keeps it (rows that do not keep it are masked
+ * inside the tile). */
 #define SOL_QUERY_TILE 128
 
 /* Bytes of device workspace sol_attn_fwd needs for this shape and block size (0 on bad input).
