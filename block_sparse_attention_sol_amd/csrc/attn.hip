@@ -33,8 +33,10 @@
 //                    Stages are pipelined by hand.  Per-stage scalar work is kept to one wave
 //                    where it can be (the CU has one scalar unit): wave 0 alone walks the union
 //                    and publishes each stage as a word in an LDS ring, and the lowest wave
-//                    without math issues the whole next-stage copy.  Each tile's walk starts at
-//                    a point that lines up the tiles running together on an XCD.  Given the
+//                    without math issues the whole next-stage copy.  A head's tiles are dealt
+//                    round-robin to the four XCDs of one half of the chip (work_item_quad), and
+//                    each tile's walk starts at a point that lines up the tiles running together
+//                    on an XCD.  Given the
 //                    tokens' latent grid, a workgroup's eight 16-row segments come from 2 frames
 //                    x 4 latent rows instead of 128 consecutive rows (seg_row): rows that keep
 //                    similar blocks, so the union each workgroup copies is smaller.
@@ -604,7 +606,7 @@ __global__ __launch_bounds__(kThreads16, 4) void sol_attn16_kernel(SparseArgs a)
   const int lane = t & 63, q = lane & 15, g = lane >> 4;
   const int64_t ntiles = (a.N + QT - 1) / QT;
   int64_t w;
-  if (!work_item(a.BH * ntiles, w)) return;
+  if (!work_item_quad(a.BH * ntiles, w)) return;
   const int64_t bh = w / ntiles;
   const int64_t tile = w % ntiles;
   const int64_t row0 = seg_row(a, tile * kWaves16 + wave);  // first row of this wave

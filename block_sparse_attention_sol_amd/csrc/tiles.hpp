@@ -470,6 +470,19 @@ __device__ __forceinline__ bool work_item(int64_t total, int64_t& w) {
   return w < total;
 }
 
+// Work item of this workgroup with the items split between the two halves of the chip: XCDs
+// 0-3 walk the first half of the items and XCDs 4-7 the second, each quad interleaving its items
+// round by round (XCD x of the quad takes every fourth item).  A head's query tiles are then
+// spread over four L2s instead of one, so at any time about half as many heads have their K/V in
+// flight, and the reuse of those K/V rows across the quad is served by the memory-side cache.
+// Every item in 0 .. 8*ceil(total/8) - 1 is hit once; returns false for the padding workgroups.
+__device__ __forceinline__ bool work_item_quad(int64_t total, int64_t& w) {
+  const int64_t per = (total + 7) / 8;
+  const int64_t x = blockIdx.x % 8;
+  w = (x / 4) * 4 * per + (int64_t)(blockIdx.x / 8) * 4 + (x % 4);
+  return w < total;
+}
+
 template <typename K>
 hipError_t set_smem(K kern, size_t bytes) {
   return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
