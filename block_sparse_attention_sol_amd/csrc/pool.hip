@@ -167,8 +167,9 @@ __global__ __launch_bounds__(64 * kPoolWaves) void pool_kv_kernel(
 // s_ij = q_i . Kbar_j / sqrt(d) the population variance over j is exactly q_i^T C q_i / d.
 // Writes g and C (fp64; C as [BH][D][D]) for the factorisation below.
 // One workgroup computes a 32 x 32 tile of C: pooled keys are staged through LDS in chunks of 64
-// blocks, each thread accumulates a 2 x 2 block of products and the two column sums.  The diagonal
-// tiles (ai == bi) also write g.
+// blocks, each thread accumulates a 2 x 2 block of products and, from the same operands, the sums
+// of its two a columns and two b columns (the threads of row 0 / column 0 of the thread grid
+// publish them).  The diagonal tiles (ai == bi) also write g.
 template <int D>
 __global__ __launch_bounds__(kThreads) void kstats_kernel(const float* __restrict__ kbar, int64_t M,
                                                           double* __restrict__ kglob,
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void kstats_kernel(const float* __restric
   const int ta = t / 16, tb = t % 16;  // rows 2 ta + {0,1}, columns 2 tb + {0,1} of the tile
   const float* kb = kbar + bh * M * D;
   double c00 = 0.0, c01 = 0.0, c10 = 0.0, c11 = 0.0;
-  double s1a = 0.0, s1b = 0.0;  // column sums (threads t < 32: a column t, b column t)
+  double sa0 = 0.0, sa1 = 0.0, sb0 = 0.0, sb1 = 0.0;  // sums of a columns 2 ta + {0,1}, b 2 tb + {0,1}
   for (int64_t j0 = 0; j0 < M; j0 += kChunk) {
     const int n = (int)((M - j0) < kChunk ? (M - j0) : kChunk);
     __syncthreads();
@@ -201,19 +202,24 @@ __global__ __launch_bounds__(kThreads) void kstats_kernel(const float* __restric
       c01 = fma(a0, b1, c01);
       c10 = fma(a1, b0, c10);
       c11 = fma(a1, b1, c11);
-    }
-    if (t < 32) {
-      for (int r = 0; r < n; ++r) {
-        s1a += sa[r][t];
-        s1b += sb[r][t];
-      }
+      sa0 += a0;
+      sa1 += a1;
+      sb0 += b0;
+      sb1 += b1;
     }
   }
   __shared__ double ga[32], gb[32];
-  if (t < 32) {
-    ga[t] = s1a / (double)M;
-    gb[t] = s1b / (double)M;
-    if (ai == bi) kglob[bh * D + 32 * ai + t] = s1a / (double)M;
+  if (tb == 0) {
+    ga[2 * ta] = sa0 / (double)M;
+    ga[2 * ta + 1] = sa1 / (double)M;
+    if (ai == bi) {
+      kglob[bh * D + 32 * ai + 2 * ta] = sa0 / (double)M;
+      kglob[bh * D + 32 * ai + 2 * ta + 1] = sa1 / (double)M;
+    }
+  }
+  if (ta == 0) {
+    gb[2 * tb] = sb0 / (double)M;
+    gb[2 * tb + 1] = sb1 / (double)M;
   }
   __syncthreads();
   const double inv_m = 1.0 / (double)M;
@@ -292,16 +298,22 @@ __global__ __launch_bounds__(kThreads) void kdeflate_kernel(const double* __rest
       for (int i = 0; i < TB; ++i) col[br * TB + i] = S[i][p % TB];
     }
     __syncthreads();
-    // |w|^2 and the remaining trace, summed by every thread in the same order (same decision)
+    // |w|^2 and the remaining trace: each wave sums all D entries, lane-strided and then by a
+    // butterfly, in the same order in every wave, so every wave takes the same decision
     const double rs = 1.0 / sqrt(dmax);
     double nw = 0.0, tr = 0.0;
-    for (int i = 0; i < D; ++i) {
+    for (int i = lane; i < D; i += 64) {
       const double di = dg[i];
       if (di != -INFINITY) {
         const double wi = i == p ? sqrt(dmax) : col[i] * rs;
         nw = fma(wi, wi, nw);
         tr += di;
       }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      nw += __shfl_xor(nw, off);
+      tr += __shfl_xor(tr, off);
     }
     if (!(nw > kDominant * (tr - nw) / (double)D)) break;  // uniform
     double wr[TB], wc[TB];
