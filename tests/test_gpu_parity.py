@@ -193,7 +193,10 @@ def test_sparse_tiny_workload(sol, beta):
                                             # last block holds 1 or 2 tokens: its pooled logit
                                             # carries ln 1 or ln 2, not ln(block)
                                             (3969, 128, 128, 0.7), (1985, 128, 64, 0.9),
-                                            (1985, 64, 64, 0.4), (3970, 64, 128, 1.0)])
+                                            (1985, 64, 64, 0.4), (3970, 64, 128, 1.0),
+                                            # d = 64 with more pooled keys per head than one
+                                            # 64-block chunk of the covariance kernel
+                                            (9000, 64, 64, 0.5)])
 def test_sparse_ragged(sol, N, d, block, beta):
     """Ragged N: partial last key block, partial last query tile, one-token inputs."""
     _log(f"sparse ragged N={N} d={d} block={block} beta={beta}")
@@ -423,7 +426,8 @@ def test_long_operating_point(sol):
 
 
 @pytest.mark.parametrize("N,d,block,beta", [(4096, 128, 128, 1.0), (4096, 128, 128, -0.5),
-                                            (3000, 64, 64, 1.5), (5000, 128, 64, 0.3)])
+                                            (3000, 64, 64, 1.5), (9000, 64, 64, 1.5),
+                                            (5000, 128, 64, 0.3)])
 def test_anisotropic_keys(sol, N, d, block, beta):
     """Keys with one strong direction that varies from block to block, queries nearly orthogonal to
     it: the pooled-key covariance has one eigenvalue ~10^4-10^5 times the rest, and each row's
