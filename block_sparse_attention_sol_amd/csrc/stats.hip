@@ -24,14 +24,45 @@ namespace solattn {
 
 namespace {
 // Row statistics: eight waves of 32 rows share the staged covariance pieces (two waves per SIMD
-// hide each other's latency; the pieces' 96 KB of LDS at d = 128 allow one workgroup per CU),
-// over up to kRowStatsPasses passes of 256 rows: fewer when that leaves too few workgroups to
-// spread over the CUs (small heads), since each pass after the first reuses the staged pieces.
+// hide each other's latency; the registers, and at d = 128 the pieces' 96 KB of LDS, allow one
+// workgroup per CU), over up to kRowStatsPasses passes of 256 rows, each pass after the first
+// reusing the staged pieces.  The pass count is chosen per launch (stats_passes).
 constexpr int kRowStatsWaves = 8;
 constexpr int kRowStatsThreads = 64 * kRowStatsWaves;
 constexpr int kRowStatsRows = 32 * kRowStatsWaves;  // rows per pass
 constexpr int kRowStatsPasses = 16;
-constexpr int64_t kRowStatsMinGroups = 512;         // workgroups wanted before passes grow
+
+// Passes per workgroup for `units` 256-row units over BH heads when `slots` workgroups run at
+// once: the count that minimises rounds x (passes + 1), a round being one workgroup in every slot
+// and the + 1 the staging of the pieces, which takes about as long as a pass; ties go to more
+// passes.  (Wan, 40 x 296 units on 256 slots: 16 passes, 760 workgroups in three rounds; LTX,
+// 32 x 24 units: 3 passes, 256 workgroups in one round, where 2 passes took two.)
+int stats_passes(int64_t BH, int64_t units_per_head, int64_t slots) {
+  int best = 1;
+  int64_t best_cost = -1;
+  for (int p = 1; p <= kRowStatsPasses; ++p) {
+    const int64_t groups = BH * ((units_per_head + p - 1) / p);
+    const int64_t cost = (groups + slots - 1) / slots * (p + 1);
+    if (best_cost < 0 || cost <= best_cost) {
+      best = p;
+      best_cost = cost;
+    }
+    if (p >= units_per_head) break;  // more passes than units change nothing
+  }
+  return best;
+}
+
+// Workgroups of `kern` that run at once on the current device (CUs x workgroups per CU); the
+// caller keeps the result per device (256 if the queries fail)
+int64_t stats_slots(const void* kern, size_t smem) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kRowStatsThreads, smem) !=
+          hipSuccess)
+    return 256;
+  return (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+}
 }  // namespace
 
 // ---------------------------------------------------------------------------------------------
@@ -193,10 +224,17 @@ static hipError_t launch_rowstats_t(const RowStatsArgs& a, hipStream_t stream) {
   auto kern = rowstats_kernel<D>;
   hipError_t err = set_smem(kern, smem);
   if (err != hipSuccess) return err;
-  // passes per workgroup: as many as keep at least kRowStatsMinGroups workgroups, 1 .. 16
-  const int64_t units = a.BH * ((a.N + kRowStatsRows - 1) / kRowStatsRows);
-  const int64_t want = (units + kRowStatsMinGroups - 1) / kRowStatsMinGroups;
-  const int passes = (int)(want < 1 ? 1 : want > kRowStatsPasses ? kRowStatsPasses : want);
+  // workgroups that run at once, per device (one cache per head dimension)
+  static int64_t slots_of[64] = {};
+  int dev = 0;
+  err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  int64_t slots = dev >= 0 && dev < 64 ? slots_of[dev] : 0;
+  if (slots <= 0) {
+    slots = stats_slots((const void*)kern, smem);
+    if (dev >= 0 && dev < 64) slots_of[dev] = slots;
+  }
+  const int passes = stats_passes(a.BH, (a.N + kRowStatsRows - 1) / kRowStatsRows, slots);
   const int64_t group_rows = (int64_t)kRowStatsRows * passes;
   const int64_t groups = (a.N + group_rows - 1) / group_rows;
   hipLaunchKernelGGL(kern, dim3((unsigned)(a.BH * groups)), dim3(kRowStatsThreads), smem, stream, a,
