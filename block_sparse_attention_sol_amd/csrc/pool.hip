@@ -186,15 +186,33 @@ __global__ __launch_bounds__(kThreads) void kstats_kernel(const float* __restric
   const float* kb = kbar + bh * M * D;
   double c00 = 0.0, c01 = 0.0, c10 = 0.0, c11 = 0.0;
   double sa0 = 0.0, sa1 = 0.0, sb0 = 0.0, sb1 = 0.0;  // sums of a columns 2 ta + {0,1}, b 2 tb + {0,1}
+  // the next chunk's pooled keys are loaded into registers while this chunk is multiplied
+  constexpr int kPer = kChunk * 32 / kThreads;  // elements of each of sa, sb per thread
+  static_assert(kPer * kThreads == kChunk * 32, "whole chunk per pass");
+  float na[kPer], nb[kPer];
+  auto fetch = [&](int64_t j0) {
+    const int n = (int)((M - j0) < kChunk ? (M - j0) : kChunk);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int idx = t + e * kThreads;
+      const int r = idx / 32, col = idx % 32;
+      na[e] = r < n ? kb[(j0 + r) * D + 32 * ai + col] : 0.f;
+      nb[e] = r < n ? kb[(j0 + r) * D + 32 * bi + col] : 0.f;
+    }
+  };
+  fetch(0);
   for (int64_t j0 = 0; j0 < M; j0 += kChunk) {
     const int n = (int)((M - j0) < kChunk ? (M - j0) : kChunk);
     __syncthreads();
-    for (int idx = t; idx < kChunk * 32; idx += kThreads) {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int idx = t + e * kThreads;
       const int r = idx / 32, col = idx % 32;
-      sa[r][col] = r < n ? (double)kb[(j0 + r) * D + 32 * ai + col] : 0.0;
-      sb[r][col] = r < n ? (double)kb[(j0 + r) * D + 32 * bi + col] : 0.0;
+      sa[r][col] = (double)na[e];
+      sb[r][col] = (double)nb[e];
     }
     __syncthreads();
+    if (j0 + kChunk < M) fetch(j0 + kChunk);
     for (int r = 0; r < n; ++r) {
       const double a0 = sa[r][2 * ta], a1 = sa[r][2 * ta + 1];
       const double b0 = sb[r][2 * tb], b1 = sb[r][2 * tb + 1];
