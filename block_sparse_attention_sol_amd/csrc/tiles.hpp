@@ -473,9 +473,10 @@ __device__ __forceinline__ bool work_item(int64_t total, int64_t& w) {
 // Work item of this workgroup with the items split between the two halves of the chip: XCDs
 // 0-3 walk the first half of the items and XCDs 4-7 the second, each quad interleaving its items
 // round by round (XCD x of the quad takes every fourth item).  A head's query tiles are then
-// spread over four L2s instead of one, so at any time about half as many heads have their K/V in
-// flight, and the reuse of those K/V rows across the quad is served by the memory-side cache.
-// Every item in 0 .. 8*ceil(total/8) - 1 is hit once; returns false for the padding workgroups.
+// spread over four L2s instead of one, so two heads have their K/V in flight instead of eight,
+// few enough for the memory-side cache to hold, and a K/V row one XCD of the quad fetched can be
+// served from there to the other three.  Every item in 0 .. 8*ceil(total/8) - 1 is hit once;
+// returns false for the padding workgroups.
 __device__ __forceinline__ bool work_item_quad(int64_t total, int64_t& w) {
   const int64_t per = (total + 7) / 8;
   const int64_t x = blockIdx.x % 8;
