@@ -401,18 +401,22 @@ def hunyuan_inputs():
 # 25% at 128-row query tiles) and for the long-video shape (8%).
 @pytest.mark.parametrize("beta", [2.539, 2.232, 1.927])
 def test_hunyuan_operating_points(sol, hunyuan_inputs, beta):
-    """HunyuanVideo shape (N=118800, last block 16 tokens), all 24 heads launched: sampled rows of
-    6 heads and the full mask of one, at each benchmarked density."""
+    """HunyuanVideo shape (N=118800, last block 16 tokens), all 24 heads launched as the benchmark
+    launches them (rows grouped by the 33x45x80 latent grid): sampled rows of 6 heads and the full
+    mask of one, at each benchmarked density."""
+    from block_sparse_attention_sol_amd import synth
     q, k, v = hunyuan_inputs
     _log(f"hunyuan beta={beta}")
     _sparse_vs_oracle(sol, q, k, v, beta, 128, rows_per_head=300, heads=[0, 5, 9, 13, 18, 23],
-                      what=f"hunyuan beta={beta}", full_mask_heads=[0])
+                      what=f"hunyuan beta={beta}", full_mask_heads=[0],
+                      grid=synth.WORKLOADS["hunyuan"].grid)
 
 
 def test_long_operating_point(sol):
-    """Long-video shape (N=219600, per-head amplitude U(1,3)) at its benchmarked beta: the first 27
-    heads of the seeded draw (which hold the smallest and the largest amplitude, heads 11 and 26),
-    sampled rows of 6 heads including those two, and the full mask of the largest-amplitude head."""
+    """Long-video shape (N=219600, per-head amplitude U(1,3)) at its benchmarked beta, rows grouped
+    by the 61x45x80 latent grid as the benchmark launches it: the first 27 heads of the seeded draw
+    (which hold the smallest and the largest amplitude, heads 11 and 26), sampled rows of 6 heads
+    including those two, and the full mask of the largest-amplitude head."""
     from block_sparse_attention_sol_amd import synth
     beta = 2.781
     w = synth.WORKLOADS["long"]
@@ -422,7 +426,7 @@ def test_long_operating_point(sol):
     _log(f"long: generating {hi + 1} heads (amplitude min at head {lo}, max at head {hi})")
     q, k, v = (t.cuda() for t in synth.generate("long", heads=hi + 1))
     _sparse_vs_oracle(sol, q, k, v, beta, 128, rows_per_head=250, heads=heads,
-                      what=f"long beta={beta}", full_mask_heads=[hi])
+                      what=f"long beta={beta}", full_mask_heads=[hi], grid=w.grid)
 
 
 @pytest.mark.parametrize("N,d,block,beta", [(4096, 128, 128, 1.0), (4096, 128, 128, -0.5),
