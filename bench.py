@@ -323,6 +323,9 @@ def main():
                     help="calibrate beta to this per-row kept density instead (the secondary "
                          "operating point)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--interleave", action="store_true",
+                    help="time each step as a sparse pass followed by a dense pass (the chip then "
+                         "starts every sparse pass at the dense kernel's lower clock)")
     ap.add_argument("--no-grid", action="store_true",
                     help="call the fused pass without the workload's latent grid (query rows in "
                          "contiguous 128-row workgroups) instead of sol_attn_fwd_grid")
@@ -445,17 +448,27 @@ def main():
         sol.dense_fwd(q, k, v, out=dout)
         dense_end[i].record()
 
-    # warm-up: dense first, so that the timed sparse passes follow sparse passes
-    for i in range(Wm):
-        dense(i)
-    for i in range(Wm):
-        sparse(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(Wm, Wm + K):
-        sparse(i)
-    for i in range(Wm, Wm + K):
-        dense(i)
+    if args.interleave:
+        for i in range(Wm):
+            sparse(i)
+            dense(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(Wm, Wm + K):
+            sparse(i)
+            dense(i)
+    else:
+        # warm-up: dense first, so that the timed sparse passes follow sparse passes
+        for i in range(Wm):
+            dense(i)
+        for i in range(Wm):
+            sparse(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(Wm, Wm + K):
+            sparse(i)
+        for i in range(Wm, Wm + K):
+            dense(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -510,6 +523,8 @@ def main():
             "row_grouping": "latent grid %dx%dx%d: 2 frames x 4 rows x 16 tokens per workgroup"
                             % tuple(grid) if grid is not None and d == 128 and grid[2] % 16 == 0
                             else "contiguous 128-row tiles",
+            "timing_order": "each sparse pass followed by a dense pass" if args.interleave
+                            else "K sparse passes, then K dense passes",
         },
         "sparse_ms": t_sparse,
         "sparse_ms_median": med(sparse_ms),
